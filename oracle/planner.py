@@ -1,0 +1,113 @@
+"""Reference work planner for split-KV MLA decode (test infrastructure).
+
+An independent Python statement of the plan rule, used to check the library's
+host planner (plan fields) and device planner (per-sequence arrays) bit for bit.
+It shares no code with the library.
+
+Where the rule comes from:
+
+* "perf(mla): chunk the non-FP4 gather_kv_b_proj over KV" (description): the
+  serial walk over the context becomes a grid axis of KV chunks; the grid is
+  sized from the longest sequence and a program whose chunk index is at or past
+  its own sequence's chunk count returns at once, so ragged batches stay correct.
+  Too few programs starve HBM (12 workgroups on a 256-CU part).
+* "HK MLA: MI35x m16x8 retune, new m16x4 kernel, page_size + mask support"
+  (Summary): heads times query tokens are stacked into one tile of rows
+  (num_heads * max_seqlen_qo of 64 or 128); metadata is sized for ``num_cu``
+  clusters, or twice that when the 64-row kernel runs at occupancy 2.
+
+The rule (all integer arithmetic):
+
+    hpg  = min(H, 128 // S)            heads per group (rows = hpg * S <= 128)
+    G    = ceil(H / hpg)               head groups
+    rows = hpg * S                     valid rows of a tile
+    TR   = 16 | 32 | 64 | 128          smallest of these >= rows; class = log2(TR/16)
+    C    = force_chunk if set, else
+           clamp(roundup(ceil(Lmax / want), 64), chunk_min[cls], chunk_max[cls])
+           with want = max(1, ceil(num_cu * wg_per_cu[cls] / (B * G)))
+    max_chunks = ceil(Lmax / C)        grid = (max_chunks, G, B)
+
+Per sequence (device half): a sequence is valid when ``S <= ctx_b <= Lmax`` and
+its page list holds at least ``ceil(ctx_b / P)`` pages; then
+``n_b = ceil(ctx_b / C)``, else ``n_b = 0`` and a status bit is set.
+``part_base_b`` is the exclusive prefix sum over ``b`` of
+``(n_b if n_b > 1 else 0) * G``: partial records of sequence b, group g, chunk c
+sit at record ``part_base_b + g * n_b + c``.
+"""
+
+from dataclasses import dataclass, field
+from typing import List
+
+BLOCK_ROWS = 64  # chunk lengths are multiples of this many cache rows
+MAX_TILE_ROWS = 128
+TILE_CLASSES = (16, 32, 64, 128)
+
+STATUS_CTX_TOO_SHORT = 1  # context_lens[b] < seqlen_qo
+STATUS_CTX_TOO_LONG = 2  # context_lens[b] > max_context_len
+STATUS_TOO_FEW_PAGES = 4  # page list shorter than ceil(ctx / page_size)
+
+
+def _cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+@dataclass
+class PlanOptions:
+    wg_per_cu: List[int] = field(default_factory=lambda: [4, 2, 2, 1])
+    chunk_min: List[int] = field(default_factory=lambda: [256, 256, 256, 1024])
+    chunk_max: List[int] = field(default_factory=lambda: [8192, 8192, 4096, 4096])
+    force_chunk: int = 0
+
+
+def reference_plan(batch, seqlen_qo, num_heads, max_context_len, num_cu, options=None):
+    """Plan fields for one call shape. Returns a dict; see the module docstring."""
+    o = options or PlanOptions()
+    B, S, H, L = int(batch), int(seqlen_qo), int(num_heads), int(max_context_len)
+    hpg = min(H, MAX_TILE_ROWS // S)
+    G = _cdiv(H, hpg)
+    rows = hpg * S
+    TR = next(t for t in TILE_CLASSES if t >= rows)
+    cls = TILE_CLASSES.index(TR)
+    if o.force_chunk:
+        C = int(o.force_chunk)
+    else:
+        want = max(1, _cdiv(num_cu * o.wg_per_cu[cls], B * G))
+        C = _cdiv(_cdiv(L, want), BLOCK_ROWS) * BLOCK_ROWS
+        C = min(max(C, o.chunk_min[cls]), o.chunk_max[cls])
+    max_chunks = _cdiv(L, C)
+    return {
+        "heads_per_group": hpg,
+        "num_groups": G,
+        "rows_per_group": rows,
+        "tile_rows": TR,
+        "tile_class": cls,
+        "chunk_len": C,
+        "max_chunks": max_chunks,
+        "grid": (max_chunks, G, B),
+        "partial_capacity_records": B * G * max_chunks,
+    }
+
+
+def device_plan_arrays(plan, seqlen_qo, max_context_len, page_size, context_lens, kv_indptr):
+    """Per-sequence chunk counts, partial bases and the status bits (device half)."""
+    S, L, P = int(seqlen_qo), int(max_context_len), int(page_size)
+    C, G = plan["chunk_len"], plan["num_groups"]
+    n_chunks, part_base = [], []
+    status = 0
+    running = 0
+    for b, ctx in enumerate(context_lens):
+        ctx = int(ctx)
+        pages = int(kv_indptr[b + 1]) - int(kv_indptr[b])
+        bad = 0
+        if ctx < S:
+            bad |= STATUS_CTX_TOO_SHORT
+        if ctx > L:
+            bad |= STATUS_CTX_TOO_LONG
+        if not bad and pages < _cdiv(ctx, P):
+            bad |= STATUS_TOO_FEW_PAGES
+        status |= bad
+        n = 0 if bad else _cdiv(ctx, C)
+        n_chunks.append(n)
+        part_base.append(running)
+        running += (n if n > 1 else 0) * G
+    return n_chunks, part_base, status

@@ -1,0 +1,80 @@
+"""Structural pins of the reference planner (CPU only)."""
+
+import numpy as np
+import pytest
+
+from oracle import PlanOptions, reference_plan, device_plan_arrays
+from oracle.planner import STATUS_CTX_TOO_SHORT, STATUS_CTX_TOO_LONG, STATUS_TOO_FEW_PAGES
+
+
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+SHAPES = [
+    # batch, S, H, Lmax
+    (2, 1, 16, 100), (64, 1, 128, 8192), (256, 1, 128, 23333), (1, 1, 12, 109440),
+    (5, 1, 12, 109440), (128, 4, 16, 5200), (3, 2, 128, 1000), (7, 8, 16, 64), (1, 3, 5, 3),
+    (9, 1, 40, 777), (4, 4, 64, 4096), (1, 1, 1, 1),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_plan_structure(shape):
+    B, S, H, L = shape
+    p = reference_plan(B, S, H, L, num_cu=256)
+    hpg, G, rows, TR, C = p["heads_per_group"], p["num_groups"], p["rows_per_group"], p["tile_rows"], p["chunk_len"]
+    assert 1 <= hpg <= H and hpg * S <= 128 and rows == hpg * S
+    assert G * hpg >= H and (G - 1) * hpg < H  # groups cover every head, no empty group
+    assert TR in (16, 32, 64, 128) and TR >= rows and (TR == 16 or TR // 2 < rows)
+    assert C % 64 == 0 and C >= 64
+    assert p["max_chunks"] * C >= L and (p["max_chunks"] - 1) * C < L
+    assert p["grid"] == (p["max_chunks"], G, B)
+
+
+def test_plan_values_for_the_benchmark_shapes():
+    # Hand-derived from the rule with the default options and 256 CUs.
+    p = reference_plan(64, 1, 128, 8192, 256)
+    assert (p["heads_per_group"], p["num_groups"], p["tile_rows"], p["chunk_len"], p["max_chunks"]) == (128, 1, 128, 2048, 4)
+    p = reference_plan(128, 4, 16, 5200, 256)
+    assert (p["heads_per_group"], p["tile_rows"], p["chunk_len"], p["max_chunks"]) == (16, 64, 1344, 4)
+    p = reference_plan(256, 1, 128, 23333, 256)
+    assert (p["chunk_len"], p["max_chunks"]) == (4096, 6)
+    p = reference_plan(1, 1, 12, 109440, 256)
+    assert (p["tile_rows"], p["chunk_len"], p["max_chunks"]) == (16, 256, 428)
+    p = reference_plan(2, 1, 16, 100, 256, PlanOptions(force_chunk=64))
+    assert (p["chunk_len"], p["max_chunks"]) == (64, 2)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_device_arrays_tile_every_context_exactly(seed):
+    rng = np.random.default_rng(seed)
+    B, S, H, P = 37, int(rng.integers(1, 5)), int(rng.integers(1, 130)), int(rng.choice([1, 16, 64]))
+    lens = rng.integers(S, 3000, size=B)
+    L = int(lens.max())
+    indptr = np.concatenate([[0], np.cumsum(_cdiv(lens, P))])
+    p = reference_plan(B, S, H, L, 256, PlanOptions(force_chunk=int(rng.choice([0, 64, 192]))))
+    n, base, status = device_plan_arrays(p, S, L, P, lens, indptr)
+    assert status == 0
+    C, G = p["chunk_len"], p["num_groups"]
+    used = set()
+    for b in range(B):
+        assert n[b] == _cdiv(int(lens[b]), C) >= 1 and n[b] <= p["max_chunks"]
+        starts = [c * C for c in range(n[b])]
+        ends = [min((c + 1) * C, int(lens[b])) for c in range(n[b])]
+        assert starts[0] == 0 and ends[-1] == lens[b]
+        assert all(e > s for s, e in zip(starts, ends)) and all(e == s2 for e, s2 in zip(ends, starts[1:]))
+        if n[b] > 1:
+            recs = {base[b] + g * n[b] + c for g in range(G) for c in range(n[b])}
+            assert not (recs & used) and len(recs) == G * n[b]
+            used |= recs
+    assert max(used, default=-1) < p["partial_capacity_records"]
+
+
+def test_device_status_bits():
+    p = reference_plan(4, 2, 8, 100, 256)
+    lens = [1, 101, 50, 50]
+    indptr = [0, 1, 102, 103, 153]  # seq 2 has 1 page of size 1 for 50 rows
+    n, base, status = device_plan_arrays(p, 2, 100, 1, lens, indptr)
+    assert status == STATUS_CTX_TOO_SHORT | STATUS_CTX_TOO_LONG | STATUS_TOO_FEW_PAGES
+    assert n[:3] == [0, 0, 0] and n[3] == _cdiv(50, p["chunk_len"])
