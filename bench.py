@@ -1,0 +1,200 @@
+"""Benchmark: MLA decode over a paged latent cache on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step = one call of the hot path (mla_decode + mla_split_combine) over the
+whole batch, inputs resident in HBM. Between steps a 1 GiB buffer is
+overwritten (outside the timed events) so that neither L2 nor the 256 MB MALL
+holds the previous call's cache rows, as in serving where other layers run in
+between. Prints one JSON line.
+
+Roofline accounting (per decode launch):
+  algorithmic bytes = sum_b ctx_b * 576 * e (each cache row read once; e = 2 bf16, 1 fp8)
+                      + B*S*H*576*2 (q) + B*S*H*512*2 (out) + 4*(B+1) + 4*pages + 4*B (page table, lengths)
+  algorithmic flops = 2 * H * (visible row visits) * (576 + 512)
+against 8 TB/s HBM and 2.5 PFLOP/s dense bf16 MFMA.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+DEFAULT_WORKLOAD = "dense_b64_h128_ctx8192_bf16"
+METRIC = "MLA decode µs/call + HBM TB/s & MFMA % peak, 128 heads ctx 8192 batch 64"
+
+
+def algorithmic_counts(case):
+    import numpy as np
+    e = 2 if case.kv_dtype == "bf16" else 1
+    ctx = case.context_lens.astype(np.int64)
+    B, S, H = case.batch, case.seqlen_qo, case.num_heads
+    rows = int(ctx.sum())
+    nbytes = rows * 576 * e + B * S * H * 576 * 2 + B * S * H * 512 * 2 + 4 * (B + 1) + 4 * int(case.kv_indptr[-1]) + 4 * B
+    if case.causal:
+        visits = int(sum(int(c) - S + 1 + s for c in ctx for s in range(S)))
+    else:
+        visits = rows * S
+    flops = 2 * H * visits * (576 + 512)
+    return nbytes, flops
+
+
+def cpu_baseline(case, budget_s=20.0):
+    """The oracle as it stands, timed on a bounded sample of sequences."""
+    import numpy as np
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    t_seq = []
+    order = list(range(case.batch))
+    t0 = time.perf_counter()
+    for b in order:
+        s0 = time.perf_counter()
+        oracle.mla_decode_reference_one(case.q_bits, case.cache_raw, case.kv_dtype, case.kv_scale, case.kv_indptr,
+                                        case.kv_page_indices, case.context_lens, case.page_size,
+                                        case.softmax_scale, case.causal, b)
+        t_seq.append((b, time.perf_counter() - s0))
+        if time.perf_counter() - t0 > budget_s:
+            break
+    done = [b for b, _ in t_seq]
+    secs = sum(t for _, t in t_seq)
+    rows_done = int(case.context_lens[done].astype(np.int64).sum())
+    rows_all = int(case.context_lens.astype(np.int64).sum())
+    per_call_us = secs * rows_all / rows_done * 1e6
+    return {"value": per_call_us, "unit": "us", "cores": cores, "kind": "oracle",
+            "sample": f"{len(done)} of {case.batch} sequences ({rows_done} cache rows, {secs:.1f} s), "
+                      f"scaled by cache rows to the full batch; float64 numpy, BLAS threads = {cores}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this decode path has no multi-GPU mode (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    if not args.no_cpu_baseline:
+        n = str(len(os.sched_getaffinity(0)))
+        for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+            os.environ[var] = n
+
+    import numpy as np
+    import torch
+
+    import mla_paged_latent_02_amd as mla
+    from mla_paged_latent_02_amd.device import Decoder, DeviceInputs
+    from mla_synth import WORKLOADS, make_case
+
+    spec = WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    case = make_case(**spec)
+    t_gen = time.perf_counter() - t_gen
+    torch.cuda.set_device(0)
+    inp = DeviceInputs.from_host(
+        q_bits=case.q_bits, cache_raw=case.cache_raw, kv_indptr=case.kv_indptr,
+        kv_page_indices=case.kv_page_indices, context_lens=case.context_lens, batch=case.batch,
+        seqlen_qo=case.seqlen_qo, num_heads=case.num_heads, page_size=case.page_size,
+        max_context_len=case.max_context_len, causal=case.causal, kv_dtype=case.kv_dtype,
+        softmax_scale=case.softmax_scale, kv_scale=case.kv_scale, num_slots=case.num_slots)
+    stream = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    dec = Decoder(inp, None, 0, stream)
+    torch.cuda.synchronize()
+    plan_us = (time.perf_counter() - t0) * 1e6
+    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        mla.decode(dec.plan, inp.q, inp.cache, inp.kv_indptr, inp.kv_page_indices, inp.context_lens, dec.out,
+                   dec.lse, dec.workspace, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        mla.split_combine(dec.plan, dec.workspace, dec.out, dec.lse, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        if flush is not None:
+            flush.fill_(1)
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    wall0 = time.perf_counter()
+    for k in range(args.steps):
+        if flush is not None:
+            flush.fill_(k & 0xFF)
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    dec_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    comb_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    call_ms = dec_ms + comb_ms
+    call_us = float(np.mean(call_ms) * 1e3)
+
+    nbytes, flops = algorithmic_counts(case)
+    dec_s = float(np.mean(dec_ms)) * 1e-3
+    achieved_gbs = nbytes / dec_s / 1e9
+    tbs_call = nbytes / (call_us * 1e-6) / 1e12
+    mfma_pct_call = flops / (call_us * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 100
+    ai = flops / nbytes
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if ai < ridge:
+        roof = {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved_gbs / HBM_PEAK_GBS}
+    else:
+        tf = flops / dec_s / 1e12
+        roof = {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": tf / MFMA_BF16_PEAK_TFLOPS}
+    roof["traffic"] = None
+    roof["kernel"] = "mla_decode_kernel"
+    roof["kernel_avg_us"] = float(np.mean(dec_ms) * 1e3)
+    roof["alg_bytes"] = nbytes
+    roof["alg_flops"] = flops
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(case)
+
+    result = {
+        "metric": METRIC,
+        "value": call_us,
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": float(np.mean(call_ms)),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if case.kv_dtype == "bf16" else "fp8-e4m3fn cache, bf16 mfma",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": case.batch, "heads": case.num_heads,
+                   "seqlen_qo": case.seqlen_qo, "max_ctx": case.max_context_len, "page_size": case.page_size,
+                   "kv_dtype": case.kv_dtype, "causal": case.causal},
+        "hbm_tb_per_s": tbs_call,
+        "mfma_pct_of_bf16_peak": mfma_pct_call,
+        "decode_us": float(np.mean(dec_ms) * 1e3),
+        "combine_us": float(np.mean(comb_ms) * 1e3),
+        "call_us_p10_p50_p90": [float(np.percentile(call_ms, q) * 1e3) for q in (10, 50, 90)],
+        "plan_us_first_call": plan_us,
+        "wall_s_timed_loop": wall,
+        "flush_between_steps": flush is not None,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

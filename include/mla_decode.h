@@ -1,0 +1,203 @@
+/*
+ * mla_decode.h — C ABI of the MI355X (gfx950) MLA decode library.
+ *
+ * Multi-head latent attention decode over a paged latent KV cache. For each
+ * sequence b, query token s and head h:
+ *
+ *   n      = ctx_b - S + 1 + s  with the causal mask, else ctx_b
+ *   slot_r = kv_page_indices[kv_indptr[b] + r / page_size] * page_size + r % page_size
+ *   K_r    = deq(cache[slot_r, 0:576]),  V_r = K_r[0:512]
+ *   z_r    = softmax_scale * (q[b,s,h,:] . K_r)          for r < n
+ *   out[b,s,h,:] = sum_r exp(z_r - max z) V_r / sum_r exp(z_r - max z)
+ *   lse[b,s,h]   = max z + ln(sum_r exp(z_r - max z))
+ *
+ * deq is exact for bf16 and (fp8 e4m3fn byte value) * kv_scale for fp8.
+ *
+ * Sources. The pages state no formula; this is the plainest reading of them:
+ *  - "HK MLA: MI35x m16x8 retune, new m16x4 kernel, page_size + mask support",
+ *    Summary: decode over a paged latent cache with a variable page size and a
+ *    causal mask for multi-token (MTP) queries; heads x query tokens stacked
+ *    into 64- or 128-row tiles; device-side metadata sized for num_cu clusters.
+ *  - "[Perf][Kimi-K3] Cut MLA decode concat/cache epilogue latency", Purpose:
+ *    the decode FMHA reads the absorbed query (ql_nope joined with q_pe) and
+ *    576-wide latent cache rows.
+ *  - "perf(mla): chunk the non-FP4 gather_kv_b_proj over KV", description:
+ *    KV-chunk grid axis sized from the longest sequence with an early exit for
+ *    chunks past a sequence's end; fp8 cache, page size 1.
+ * Row layout (latent 512 first, then rope 64), the fp8 flavour (OCP e4m3fn,
+ * max 448), the scale 1/sqrt(192) used by the workloads and the split-KV
+ * log-sum-exp merge are readings, not statements of the pages.
+ *
+ * Conventions for every entry point:
+ *  - All pointers named d_* are device pointers (HIP device memory of the
+ *    current device); everything else is host memory. The caller owns every
+ *    buffer; the library never allocates or frees device memory, and never
+ *    synchronises the stream (except mla_debug_read_plan_arrays).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work
+ *    is enqueued in call order; the library keeps no state between calls.
+ *  - Host-detectable errors are returned before any device work is enqueued.
+ *    Device-detectable errors (bad context length, short page list, page
+ *    index out of range) set bits in the status word of the workspace; the
+ *    kernels clamp every index and never read out of bounds.
+ *  - Returns MLA_ERR_HIP if a launch reports an error.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+#define MLA_ROW_DIM 576    /* q / cache row width: 512 latent + 64 rope */
+#define MLA_LATENT_DIM 512 /* V width = output width */
+#define MLA_MAX_SEQLEN_QO 8
+#define MLA_PLAN_MAGIC 0x4d4c4131u
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,         /* null pointer, non-positive size, bad enum */
+  MLA_ERR_UNSUPPORTED = 2,         /* valid but outside the supported shapes */
+  MLA_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes < plan->ws_bytes */
+  MLA_ERR_HIP = 4,                 /* the HIP runtime reported an error */
+  MLA_ERR_BAD_PLAN = 5             /* plan not made by mla_decode_plan* */
+} mla_status_t;
+
+typedef enum { MLA_KV_BF16 = 0, MLA_KV_FP8_E4M3FN = 1 } mla_kv_dtype_t;
+
+/* Status-word bits written to the workspace by the device (see ws_status_offset). */
+#define MLA_DEV_CTX_TOO_SHORT 1u    /* context_lens[b] < seqlen_qo      */
+#define MLA_DEV_CTX_TOO_LONG 2u     /* context_lens[b] > max_context_len */
+#define MLA_DEV_TOO_FEW_PAGES 4u    /* page list shorter than ceil(ctx/page_size) */
+#define MLA_DEV_PAGE_OUT_OF_RANGE 8u /* a page index >= num_slots / page_size (or < 0) */
+
+/* Shape and numeric parameters of one decode call. */
+typedef struct {
+  int32_t batch;           /* B >= 1 */
+  int32_t seqlen_qo;       /* S, 1..8 query tokens per sequence */
+  int32_t num_heads;       /* H >= 1 */
+  int32_t page_size;       /* P >= 1 cache rows per page */
+  int32_t max_context_len; /* upper bound of context_lens (sizes the grid and workspace) */
+  int32_t causal;          /* 0 or 1: token s sees ctx - S + 1 + s rows */
+  int32_t kv_dtype;        /* mla_kv_dtype_t */
+  float softmax_scale;     /* multiplies q . k */
+  float kv_scale;          /* fp8: per-tensor dequant scale; bf16: must be 1 */
+  int64_t num_slots;       /* rows in the cache pool; a multiple of page_size */
+} mla_decode_params_t;
+
+/* Tunables of the work split, per tile class (tile rows 16, 32, 64, 128). */
+typedef struct {
+  int32_t wg_per_cu[4]; /* target workgroups per CU */
+  int32_t chunk_min[4]; /* chunk length bounds in cache rows, multiples of 64 */
+  int32_t chunk_max[4];
+  int32_t force_chunk;  /* 0 = use the rule; else this chunk length (multiple of 64) */
+} mla_plan_options_t;
+
+/* Host copy of a plan. Made by mla_decode_plan / mla_decode_plan_host; read-only for callers. */
+typedef struct {
+  uint32_t magic;
+  int32_t num_cu;
+  mla_decode_params_t params;
+  mla_plan_options_t options;
+  int32_t heads_per_group; /* hpg = min(H, 128 / S) */
+  int32_t num_groups;      /* G = ceil(H / hpg) */
+  int32_t rows_per_group;  /* hpg * S valid rows per tile */
+  int32_t tile_rows;       /* 16, 32, 64 or 128 */
+  int32_t tile_class;      /* log2(tile_rows / 16) */
+  int32_t chunk_len;       /* C, cache rows per workgroup, multiple of 64 */
+  int32_t max_chunks;      /* ceil(max_context_len / C) */
+  int32_t grid[3];         /* decode grid: (max_chunks, G, B) */
+  int64_t partial_capacity_records; /* B * G * max_chunks */
+  uint64_t ws_status_offset;   /* uint32 status word (+ reserved), bytes from workspace start */
+  uint64_t ws_nchunks_offset;  /* int32 [B]: chunks of each sequence (0 = invalid sequence) */
+  uint64_t ws_partbase_offset; /* int32 [B]: first partial record of each sequence */
+  uint64_t ws_part_out_offset; /* float [records][rows_per_group][512]: normalised partial outputs */
+  uint64_t ws_part_lse_offset; /* float [records][rows_per_group]: partial lse, base-2 log */
+  uint64_t ws_bytes;           /* total workspace bytes needed */
+} mla_plan_t;
+
+/* ABI version of the loaded library (MLA_ABI_VERSION). */
+int32_t mla_abi_version(void);
+
+/* Human-readable text of a status code (static storage). */
+const char* mla_status_string(mla_status_t status);
+
+/* Fills *out with the default tunables. */
+void mla_plan_options_default(mla_plan_options_t* out);
+
+/*
+ * Host half of the planner: validates params and computes the plan (tile
+ * grouping, chunk length, grid, workspace layout) with no device work and no
+ * HIP call when num_cu > 0. num_cu <= 0 asks the current device for its CU
+ * count. options may be NULL (defaults). Rule ("perf(mla): chunk the non-FP4
+ * gather_kv_b_proj over KV", description: chunk grid from the longest
+ * sequence; "HK MLA ..." Summary: rows = heads x query tokens, num_cu clusters):
+ *   hpg = min(H, 128/S); G = ceil(H/hpg); TR = smallest of 16/32/64/128 >= hpg*S
+ *   C = force_chunk or clamp(roundup(ceil(Lmax / want), 64), chunk_min, chunk_max),
+ *       want = max(1, ceil(num_cu * wg_per_cu / (B*G)))
+ *   max_chunks = ceil(Lmax / C), grid = (max_chunks, G, B)
+ */
+mla_status_t mla_decode_plan_host(const mla_decode_params_t* params, const mla_plan_options_t* options,
+                                  int32_t num_cu, mla_plan_t* out_plan);
+
+/* Workspace bytes for a call shape (0 if params or options are invalid). */
+size_t mla_decode_workspace_size(const mla_decode_params_t* params, const mla_plan_options_t* options,
+                                 int32_t num_cu);
+
+/*
+ * Full planner: the host half above, then one device launch that, per
+ * sequence, validates context_lens[b] (S <= ctx <= max_context_len, enough
+ * pages), writes n_b = ceil(ctx_b / C) (0 if invalid), the exclusive prefix
+ * sum of partial records, and the status word. d_context_lens [B] and
+ * d_kv_indptr [B+1] are int32 device arrays. The device arrays stay valid for
+ * every mla_decode / mla_split_combine call with the same context lengths.
+ */
+mla_status_t mla_decode_plan(const mla_decode_params_t* params, const mla_plan_options_t* options,
+                             int32_t num_cu, const int32_t* d_context_lens, const int32_t* d_kv_indptr,
+                             void* d_workspace, size_t workspace_bytes, void* stream, mla_plan_t* out_plan);
+
+/*
+ * Decode attention over the paged cache. One workgroup per (chunk, head group,
+ * sequence); a workgroup whose chunk is past its sequence's n_b exits at once.
+ *   d_q              bf16 [B, S, H, 576], contiguous
+ *   d_kv_cache       [num_slots, 576] bf16 or fp8 e4m3fn bytes, contiguous
+ *   d_kv_indptr      int32 [B+1]: page list of b is d_kv_page_indices[indptr[b] .. indptr[b+1])
+ *   d_kv_page_indices int32 page ids (page p holds slots p*P .. p*P+P-1)
+ *   d_context_lens   int32 [B]
+ *   d_out            bf16 [B, S, H, 512]: written for sequences with n_b == 1;
+ *                    sequences with n_b > 1 are written by mla_split_combine;
+ *                    invalid sequences are filled with NaN
+ *   d_lse            float [B, S, H] natural-log lse, or NULL
+ *   d_workspace      the workspace given to mla_decode_plan
+ */
+mla_status_t mla_decode(const mla_plan_t* plan, const void* d_q, const void* d_kv_cache,
+                        const int32_t* d_kv_indptr, const int32_t* d_kv_page_indices,
+                        const int32_t* d_context_lens, void* d_out, float* d_lse, void* d_workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * Log-sum-exp merge of split-KV partials: for every (b, s, h) of a sequence
+ * with n_b > 1, with M = max_c lse_c and w_c = 2^(lse_c - M) (partials hold
+ * base-2 lse), out = bf16(sum_c w_c o_c / sum_c w_c) and lse = (M + log2 sum_c w_c) * ln 2.
+ * Partials with lse = -inf (no visible rows) weigh 0. The pages describe no
+ * merge; this is the standard identity for a softmax split over disjoint rows.
+ * Sequences with n_b <= 1 are left untouched.
+ */
+mla_status_t mla_split_combine(const mla_plan_t* plan, void* d_workspace, size_t workspace_bytes,
+                               void* d_out, float* d_lse, void* stream);
+
+/*
+ * Test hook: synchronously copies the planner's device arrays to host memory
+ * (any pointer may be NULL). h_nchunks and h_partbase hold B int32 each.
+ */
+mla_status_t mla_debug_read_plan_arrays(const mla_plan_t* plan, const void* d_workspace,
+                                        int32_t* h_nchunks, int32_t* h_partbase, uint32_t* h_status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

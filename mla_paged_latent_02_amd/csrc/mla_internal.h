@@ -1,0 +1,64 @@
+// Internal declarations shared by the host planner, the C-ABI layer and the kernels.
+#pragma once
+
+#include <cstdint>
+
+#include "mla_decode.h"
+
+namespace mla {
+
+constexpr int kRowDim = MLA_ROW_DIM;       // 576
+constexpr int kLatentDim = MLA_LATENT_DIM; // 512
+constexpr int kBlockRows = 64;             // cache rows per pipeline block; chunks are multiples
+constexpr int kMaxTileRows = 128;
+constexpr int kMaxSeqlenQo = MLA_MAX_SEQLEN_QO;
+
+// Everything one decode launch needs, passed by value.
+struct DecodeArgs {
+  const uint16_t* q;            // bf16 [B, S, H, 576]
+  const uint8_t* cache;         // [num_slots, 576] elements of 2 (bf16) or 1 (fp8) bytes
+  const int32_t* kv_indptr;     // [B+1]
+  const int32_t* kv_page_indices;
+  const int32_t* context_lens;  // [B]
+  const int32_t* nchunks;       // [B] from the planner
+  const int32_t* partbase;      // [B] from the planner
+  uint32_t* status;             // status word
+  uint16_t* out;                // bf16 [B, S, H, 512]
+  float* lse;                   // [B, S, H] or null
+  float* part_out;              // [records][rows][512]
+  float* part_lse;              // [records][rows]
+  int64_t num_pages;            // num_slots / page_size
+  int32_t batch, seqlen_qo, num_heads, page_size;
+  int32_t heads_per_group, num_groups, rows_per_group, chunk_len;
+  int32_t causal;
+  float score_scale_log2;       // softmax_scale * kv_scale * log2(e)
+  float out_scale;              // kv_scale
+};
+
+struct CombineArgs {
+  const int32_t* nchunks;
+  const int32_t* partbase;
+  const float* part_out;
+  const float* part_lse;
+  uint16_t* out;
+  float* lse;
+  int32_t batch, seqlen_qo, num_heads, heads_per_group, num_groups, rows_per_group;
+  int32_t cols_per_wg;  // 512 / column blocks
+};
+
+struct PlanArgs {
+  const int32_t* context_lens;
+  const int32_t* kv_indptr;
+  int32_t* nchunks;
+  int32_t* partbase;
+  uint32_t* status;
+  int32_t batch, seqlen_qo, max_context_len, page_size, chunk_len, num_groups;
+};
+
+// Launchers (mla_kernels.hip). Return hipError_t as int.
+int launch_plan(const PlanArgs& a, void* stream);
+int launch_decode(const DecodeArgs& a, int kv_dtype, int tile_class, int grid_x, int grid_y, int grid_z,
+                  void* stream);
+int launch_combine(const CombineArgs& a, int max_chunks, void* stream);
+
+}  // namespace mla

@@ -1,0 +1,141 @@
+"""The C ABI loads and exports every declared symbol; host planning and argument
+checks behave (CPU only: no call here touches a GPU)."""
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import mla_paged_latent_02_amd as mla
+from oracle import PlanOptions as RefOptions, reference_plan
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == set(mla.EXPORTED)
+    for n in names:
+        assert hasattr(mla.lib(), n), n
+
+
+def test_struct_layouts_match_the_c_compiler(tmp_path):
+    # sizeof/offsetof as gcc lays out the header, against the ctypes mirrors
+    checks = [("mla_decode_params_t", mla.DecodeParams), ("mla_plan_options_t", mla.PlanOptions),
+              ("mla_plan_t", mla.Plan)]
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "mla_decode.h"', "int main(void) {"]
+    for cname, cls in checks:
+        lines.append(f'printf("%zu\\n", sizeof({cname}));')
+        for f, _ in cls._fields_:
+            lines.append(f'printf("%zu\\n", offsetof({cname}, {f}));')
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    want = []
+    for _, cls in checks:
+        want.append(ctypes.sizeof(cls))
+        want += [getattr(cls, f).offset for f, _ in cls._fields_]
+    assert got == want
+
+
+def test_abi_version_and_status_strings():
+    assert mla.abi_version() == 1
+    for code in range(6):
+        assert mla.lib().mla_status_string(code)
+    assert mla.lib().mla_status_string(99) == b"unknown status"
+
+
+def params(**kw):
+    base = dict(batch=4, seqlen_qo=1, num_heads=16, page_size=16, max_context_len=1000, causal=False,
+                kv_dtype="fp8_e4m3fn", softmax_scale=1 / math.sqrt(192), kv_scale=0.01, num_slots=4096)
+    base.update(kw)
+    return mla.make_params(**base)
+
+
+SHAPES = [(2, 1, 16, 100), (64, 1, 128, 8192), (256, 1, 128, 23333), (1, 1, 12, 109440), (5, 1, 12, 109440),
+          (128, 4, 16, 5200), (3, 2, 128, 1000), (7, 8, 16, 64), (1, 3, 5, 3), (9, 1, 40, 777), (4, 4, 64, 4096)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("force", [0, 64, 320])
+def test_host_plan_matches_reference_planner_bit_exactly(shape, force):
+    B, S, H, L = shape
+    p = params(batch=B, seqlen_qo=S, num_heads=H, max_context_len=L)
+    plan = mla.plan_host(p, mla.make_options(force_chunk=force), num_cu=256)
+    ref = reference_plan(B, S, H, L, 256, RefOptions(force_chunk=force))
+    got = mla.plan_to_dict(plan)
+    assert got == {k: ref[k] for k in got}
+    assert plan.magic == 0x4D4C4131
+    # workspace layout: 256-aligned, disjoint, in order, large enough for every partial
+    offs = [plan.ws_status_offset, plan.ws_nchunks_offset, plan.ws_partbase_offset, plan.ws_part_out_offset,
+            plan.ws_part_lse_offset, plan.ws_bytes]
+    assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
+    assert plan.ws_nchunks_offset - plan.ws_status_offset >= 16
+    assert plan.ws_partbase_offset - plan.ws_nchunks_offset >= 4 * B
+    assert plan.ws_part_lse_offset - plan.ws_part_out_offset >= 4 * 512 * ref["rows_per_group"] * ref["partial_capacity_records"]
+    assert plan.ws_bytes - plan.ws_part_lse_offset >= 4 * ref["rows_per_group"] * ref["partial_capacity_records"]
+    assert mla.workspace_size(p, mla.make_options(force_chunk=force), 256) == plan.ws_bytes
+
+
+def test_non_default_options_follow_the_rule():
+    o = mla.make_options(wg_per_cu=[1, 1, 1, 3], chunk_min=[64, 64, 64, 64], chunk_max=[128, 128, 128, 512])
+    ro = RefOptions(wg_per_cu=[1, 1, 1, 3], chunk_min=[64, 64, 64, 64], chunk_max=[128, 128, 128, 512])
+    for shape in SHAPES:
+        B, S, H, L = shape
+        got = mla.plan_to_dict(mla.plan_host(params(batch=B, seqlen_qo=S, num_heads=H, max_context_len=L), o, 304))
+        ref = reference_plan(B, S, H, L, 304, ro)
+        assert got == {k: ref[k] for k in got}
+
+
+@pytest.mark.parametrize("bad, code", [
+    (dict(batch=0), 1), (dict(seqlen_qo=0), 1), (dict(seqlen_qo=9), 2), (dict(num_heads=0), 1),
+    (dict(page_size=0), 1), (dict(max_context_len=0), 1), (dict(causal=2), 1), (dict(kv_dtype=7), 1),
+    (dict(softmax_scale=float("nan")), 1), (dict(softmax_scale=0.0), 1), (dict(kv_scale=0.0), 1),
+    (dict(kv_scale=-1.0), 1), (dict(kv_dtype="bf16", kv_scale=0.5), 1), (dict(num_slots=0), 1),
+    (dict(num_slots=4097), 1), (dict(batch=70000), 2), (dict(seqlen_qo=4, max_context_len=3), 1),
+])
+def test_invalid_params_are_rejected_before_device_work(bad, code):
+    p = params(**bad)
+    with pytest.raises(mla.MlaError) as e:
+        mla.plan_host(p, None, num_cu=256)
+    assert e.value.status == code
+    assert mla.workspace_size(p, None, 256) == 0
+
+
+@pytest.mark.parametrize("opt", [dict(force_chunk=63), dict(force_chunk=-64), dict(chunk_min=[0, 64, 64, 64]),
+                                 dict(chunk_max=[32, 64, 64, 64]), dict(wg_per_cu=[0, 1, 1, 1])])
+def test_invalid_options_are_rejected(opt):
+    with pytest.raises(mla.MlaError) as e:
+        mla.plan_host(params(), mla.make_options(**opt), num_cu=256)
+    assert e.value.status == 1
+
+
+def test_entry_points_reject_null_and_bad_plans_without_touching_the_device():
+    lib = mla.lib()
+    p = params()
+    plan = mla.Plan()
+    # null pointers -> invalid argument, before any HIP call
+    assert lib.mla_decode_plan(ctypes.byref(p), None, 256, None, None, None, 0, None, ctypes.byref(plan)) == 1
+    # a zeroed plan is not a plan
+    assert lib.mla_decode(ctypes.byref(plan), *([None] * 8), 0, None) == 5
+    assert lib.mla_split_combine(ctypes.byref(plan), None, 0, None, None, None) == 5
+    assert lib.mla_debug_read_plan_arrays(ctypes.byref(plan), None, None, None, None) == 5
+    good = mla.plan_host(p, None, 256)
+    fake = ctypes.c_void_p(16)  # never dereferenced: rejected by the size check first
+    assert lib.mla_decode(ctypes.byref(good), fake, fake, fake, fake, fake, fake, None, fake, 0, None) == 3
+    assert lib.mla_decode(ctypes.byref(good), None, fake, fake, fake, fake, fake, None, fake,
+                          good.ws_bytes, None) == 1
+    assert lib.mla_split_combine(ctypes.byref(good), fake, 0, fake, None, None) == 3

@@ -1,0 +1,205 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, on MI355X.
+
+Tolerance (from the accuracy target of this path: bf16 output, fp32 accumulate):
+|gpu - oracle| <= 1e-2 + 1e-2 |oracle| elementwise, for the output and the lse.
+Plan metadata must match the reference planner bit for bit. Output and
+workspace buffers are poisoned with NaN before every call, so any element the
+kernels fail to write fails the comparison.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mla_synth import WORKLOADS, make_case
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 1e-2
+RTOL = 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import mla_paged_latent_02_amd  # noqa: F401  (fails loudly if the library is missing)
+    yield
+
+
+def upload(case):
+    from mla_paged_latent_02_amd.device import DeviceInputs
+    return DeviceInputs.from_host(
+        q_bits=case.q_bits, cache_raw=case.cache_raw, kv_indptr=case.kv_indptr,
+        kv_page_indices=case.kv_page_indices, context_lens=case.context_lens, batch=case.batch,
+        seqlen_qo=case.seqlen_qo, num_heads=case.num_heads, page_size=case.page_size,
+        max_context_len=case.max_context_len, causal=case.causal, kv_dtype=case.kv_dtype,
+        softmax_scale=case.softmax_scale, kv_scale=case.kv_scale, num_slots=case.num_slots)
+
+
+def run(case, options=None, inputs=None):
+    from mla_paged_latent_02_amd.device import Decoder
+    inp = inputs or upload(case)
+    dec = Decoder(inp, options, poison=True)
+    out, lse = dec()
+    torch.cuda.synchronize()
+    return dec, out.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def reference(case, batches=None):
+    return oracle.mla_decode_reference(case.q_bits, case.cache_raw, case.kv_dtype, case.kv_scale, case.kv_indptr,
+                                       case.kv_page_indices, case.context_lens, case.page_size,
+                                       case.softmax_scale, case.causal, batches=batches)
+
+
+def assert_close(case, out, lse, batches=None, label=""):
+    ref_out, ref_lse = reference(case, batches)
+    bs = range(case.batch) if batches is None else batches
+    for b in bs:
+        err = np.abs(out[b] - ref_out[b])
+        bound = ATOL + RTOL * np.abs(ref_out[b])
+        bad = ~(err <= bound)
+        assert not bad.any(), (f"{label} b={b}: {int(bad.sum())} output elements out of tolerance, "
+                               f"max err {np.nanmax(err):.3g}, first at {np.argwhere(bad)[0]}")
+        lerr = np.abs(lse[b] - ref_lse[b])
+        assert np.all(lerr <= ATOL + RTOL * np.abs(ref_lse[b])), f"{label} b={b}: lse max err {np.nanmax(lerr):.3g}"
+
+
+def check_plan_arrays(case, dec):
+    import mla_paged_latent_02_amd as mla
+    n, base, status = mla.read_plan_arrays(dec.plan, dec.workspace)
+    ref = oracle.reference_plan(case.batch, case.seqlen_qo, case.num_heads, case.max_context_len,
+                                dec.plan.num_cu, _ref_options(dec.plan))
+    assert mla.plan_to_dict(dec.plan) == {k: ref[k] for k in mla.plan_to_dict(dec.plan)}
+    rn, rbase, rstatus = oracle.device_plan_arrays(ref, case.seqlen_qo, case.max_context_len, case.page_size,
+                                                   case.context_lens, case.kv_indptr)
+    assert n == rn and base == rbase and status == rstatus
+    return status
+
+
+def _ref_options(plan):
+    o = plan.options
+    return oracle.PlanOptions(list(o.wg_per_cu), list(o.chunk_min), list(o.chunk_max), o.force_chunk)
+
+
+def options(force_chunk=0):
+    import mla_paged_latent_02_amd as mla
+    return mla.make_options(force_chunk=force_chunk)
+
+
+# ------------------------------------------------------------------ small cases, full comparison
+
+def test_tiny_workload_default_plan():
+    case = make_case(**WORKLOADS["tiny_b2_h16"])
+    dec, out, lse = run(case)
+    assert check_plan_arrays(case, dec) == 0
+    assert dec.plan.max_chunks == 1
+    assert_close(case, out, lse, label="tiny")
+
+
+def test_tiny_workload_forced_split_exercises_the_combine():
+    case = make_case(**WORKLOADS["tiny_b2_h16"])
+    dec, out, lse = run(case, options(force_chunk=64))
+    check_plan_arrays(case, dec)
+    n, _, _ = __import__("mla_paged_latent_02_amd").read_plan_arrays(dec.plan, dec.workspace)
+    assert n == [1, 2]
+    assert_close(case, out, lse, label="tiny split")
+
+
+GRID = []
+for kv_dtype in ("bf16", "fp8_e4m3fn"):
+    for (S, H, causal) in ((1, 12, False), (1, 16, False), (4, 16, True), (2, 32, False), (1, 128, False),
+                           (4, 32, True), (3, 5, True), (1, 40, False)):
+        for P in (1, 16, 64):
+            GRID.append((kv_dtype, S, H, causal, P))
+
+
+@pytest.mark.parametrize("kv_dtype,S,H,causal,P", GRID)
+def test_boundary_grid(kv_dtype, S, H, causal, P):
+    C = 128
+    ctx = [max(S, c) for c in (1, 63, 64, 65, C - 1, C, C + 1, 2 * C + 1)]
+    seed = 1000 + GRID.index((kv_dtype, S, H, causal, P))
+    case = make_case(batch=len(ctx), seqlen_qo=S, num_heads=H, ctx=ctx, page_size=P, kv_dtype=kv_dtype,
+                     causal=causal, seed=seed, pool_pages=sum(-(-c // P) for c in ctx) + 3)
+    for force in (0, C):
+        dec, out, lse = run(case, options(force_chunk=force))
+        check_plan_arrays(case, dec)
+        assert_close(case, out, lse, label=f"grid force={force}")
+
+
+def test_run_to_run_bitwise_determinism():
+    case = make_case(batch=3, seqlen_qo=4, num_heads=16, ctx=[700, 5, 1300], page_size=16, kv_dtype="fp8_e4m3fn",
+                     causal=True, seed=77)
+    inp = upload(case)
+    _, o1, l1 = run(case, options(force_chunk=256), inputs=inp)
+    _, o2, l2 = run(case, options(force_chunk=256), inputs=inp)
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+    assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
+
+
+def test_invalid_sequences_get_nan_rows_and_status_bits():
+    import mla_paged_latent_02_amd as mla
+    case = make_case(batch=4, seqlen_qo=2, num_heads=16, ctx=[40, 1, 90, 33], page_size=16, kv_dtype="bf16",
+                     seed=78, max_context_len=80)
+    dec, out, lse = run(case, options(force_chunk=64))
+    n, _, status = mla.read_plan_arrays(dec.plan, dec.workspace)
+    assert status == (mla.DEV_CTX_TOO_SHORT | mla.DEV_CTX_TOO_LONG)
+    assert n[1] == 0 and n[2] == 0
+    assert np.isnan(out[1]).all() and np.isnan(out[2]).all()
+    assert np.isnan(lse[1]).all() and np.isnan(lse[2]).all()
+    assert_close(case, out, lse, batches=[0, 3], label="valid rows next to invalid ones")
+
+
+def test_short_page_list_and_bad_page_ids_are_flagged_not_read():
+    import mla_paged_latent_02_amd as mla
+    case = make_case(batch=3, seqlen_qo=1, num_heads=16, ctx=[50, 70, 20], page_size=16, kv_dtype="fp8_e4m3fn",
+                     seed=79)
+    # sequence 1: a page id past the pool (the kernel must clamp it and raise a flag)
+    good = case.kv_page_indices.copy()
+    case.kv_page_indices[case.kv_indptr[1]] = case.num_slots // 16 + 5
+    dec, out, lse = run(case)
+    _, _, status = mla.read_plan_arrays(dec.plan, dec.workspace)
+    assert status & mla.DEV_PAGE_OUT_OF_RANGE
+    case.kv_page_indices = good
+    assert_close(case, out, lse, batches=[0, 2], label="bad page id in another sequence")
+    # sequence 2: a page list one page short of its context length
+    case2 = make_case(batch=2, seqlen_qo=1, num_heads=16, ctx=[50, 40], page_size=16, kv_dtype="fp8_e4m3fn", seed=80)
+    case2.kv_indptr = case2.kv_indptr.copy()
+    case2.kv_indptr[2] -= 1
+    dec, out, lse = run(case2)
+    n, _, status = mla.read_plan_arrays(dec.plan, dec.workspace)
+    assert status == mla.DEV_TOO_FEW_PAGES and n[1] == 0 and np.isnan(out[1]).all()
+    assert_close(case2, out, lse, batches=[0], label="short page list next door")
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled outputs
+
+def _sampled(name, sample):
+    case = make_case(**WORKLOADS[name])
+    dec, out, lse = run(case)
+    check_plan_arrays(case, dec)
+    batches = sorted(set(sample(case)))
+    assert_close(case, out, lse, batches=batches, label=name)
+
+
+def test_dense_b64_h128_ctx8192_bf16_sampled():
+    _sampled("dense_b64_h128_ctx8192_bf16", lambda c: [0, 1, 31, 62, 63])
+
+
+def test_ragged_b256_h128_fp8_p64_sampled():
+    def pick(c):
+        order = np.argsort(c.context_lens)
+        return [int(order[0]), int(order[1]), int(order[128]), int(order[-2]), int(order[-1]), 0, 255]
+    _sampled("ragged_b256_h128_fp8_p64", pick)
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5])
+def test_longctx_h12_ctx109440_fp8(b):
+    _sampled(f"longctx_b{b}_h12_ctx109440_fp8", lambda c: range(c.batch))
+
+
+def test_causal_mtp4_b128_h16_ctx5200_fp8_p16_sampled():
+    _sampled("causal_mtp4_b128_h16_ctx5200_fp8_p16", lambda c: [0, 1, 64, 126, 127])
