@@ -36,6 +36,9 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2_t;
 
 #define LDS_PTR(T) __attribute__((address_space(3))) T*
+#ifndef MLA_STEP_BARRIER
+#define MLA_STEP_BARRIER() __builtin_amdgcn_sched_barrier(0)
+#endif
 
 constexpr float kLn2 = 0.6931471805599453f;
 // Lazy rescaling: the running reference max of a row moves only when a new
@@ -147,10 +150,11 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(PlanArgs a) {
 //   tail region: row r at kTailBase + r*kTailBytes holds the 64 rope elements
 //                (16-byte slots, physical slot p holds logical slot
 //                p ^ (r % kTailSlots)).
-// Row permutation: the 16 MFMA rows of a K tile read LDS rows pi(m) =
-// (m >> 2) + 4 (m & 3), so score row 4g + r of a tile is cache row g + 4r and
-// the four rows that one 16-lane group reads in a transposed V access are 4
-// rows apart (distinct banks).
+// Row permutations: MFMA row m = 4g + r (g = m/4) of K tile nt reads LDS row
+// nt*16 + pi_{nt&1}(m), pi_0(m) = 2r + 8(g&1) + (g>>1), pi_1(m) = pi_0(m) ^ 1.
+// So each 32-lane half of a transposed V read (tiles 2u, 2u+1) touches rows
+// that fall in distinct bank groups, and a K read touches 16 distinct rows.
+// Tail slots are swizzled with the row bits above the bank-group bit(s).
 template <bool FP8>
 struct RowLayout {
   static constexpr int kElem = FP8 ? 1 : 2;
@@ -161,6 +165,11 @@ struct RowLayout {
   static constexpr int kTailSlots = kTailBytes / 16;     // 4 or 8
   static constexpr int kTailBase = kBlockRows * kMainStride;
   static constexpr int kBlockBytes = kTailBase + kBlockRows * kTailBytes;
+  // physical tail slot p of row r holds logical slot p ^ tail_xor(r): the tail
+  // row stride spans kTailBytes/4 banks, so the row bits above that pick the xor
+  static __device__ __forceinline__ int tail_xor(int r) {
+    return FP8 ? ((r >> 2) & 3) : ((r >> 1) & 7);
+  }
 };
 
 template <bool FP8, int NW>
@@ -187,12 +196,17 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory");
 }
 
-// One wave = one 16-row head tile: its query rows (72 registers of bf16
-// fragments) and its 16 x 512 fp32 output (128 registers) stay in registers
-// for the whole chunk, which leaves room for two waves per SIMD. NW waves
-// share each 64-row KV block in LDS.
-template <bool FP8, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__device__ __forceinline__ int perm_row(int m, int odd) {
+  const int g = m >> 2, r = m & 3;
+  return (2 * r + 8 * (g & 1) + (g >> 1)) ^ odd;
+}
+
+// One wave = HT head tiles of 16 rows: their query fragments (72 registers
+// per tile) and their 16 x 512 fp32 outputs (128 registers per tile) stay in
+// registers for the whole chunk. NW waves share each 64-row KV block in LDS;
+// one wave per SIMD (WPE = 1) leaves room for deep LDS prefetch.
+template <bool FP8, int NW, int HT, int WPE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void mla_decode_kernel(DecodeArgs a) {
   using Cfg = DecodeCfg<FP8, NW>;
   using L = RowLayout<FP8>;
@@ -205,7 +219,7 @@ void mla_decode_kernel(DecodeArgs a) {
   const int b = blockIdx.z;
   const int n_b = a.nchunks[b];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keep it scalar
   const int i16 = lane & 15;  // MFMA column: head row within the wave's 16-row tile
   const int g4 = lane >> 4;   // MFMA k-group
 
@@ -232,34 +246,46 @@ void mla_decode_kernel(DecodeArgs a) {
   const int64_t page_base = a.kv_indptr[b];
   const int P = a.page_size;
 
-  // ---- this lane's tile row and its visible limit
-  const int rr = wave * 16 + i16;
-  const int tok = rr / a.heads_per_group;
-  const int head = grp * a.heads_per_group + rr % a.heads_per_group;
-  const bool row_ok = rr < a.rows_per_group && head < a.num_heads;
-  const int vis_end = min(c_end, a.causal ? ctx - a.seqlen_qo + 1 + tok : ctx);
-  const int row_out = row_ok ? (int)(((int64_t)b * a.seqlen_qo + tok) * a.num_heads + head) : 0;
+  // ---- this lane's tile rows (one per head tile) and their visible limits
+  int vis_end[HT], row_out[HT], row_rr[HT];
+  bool row_ok[HT];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const int rr = (wave * HT + ht) * 16 + i16;
+    const int tok = rr / a.heads_per_group;
+    const int head = grp * a.heads_per_group + rr % a.heads_per_group;
+    row_rr[ht] = rr;
+    row_ok[ht] = rr < a.rows_per_group && head < a.num_heads;
+    vis_end[ht] = min(c_end, a.causal ? ctx - a.seqlen_qo + 1 + tok : ctx);
+    row_out[ht] = row_ok[ht] ? (int)(((int64_t)b * a.seqlen_qo + tok) * a.num_heads + head) : 0;
+  }
 
   // ---- query fragments (B operand of S^T = K Q^T), resident for the whole chunk.
   // bf16 cache: fragment t holds d = 32t + 8*g4 .. +7.
   // fp8 cache:  fragment 2p+h holds d = 64p + 16*g4 + 8h .. +7 (one 16-byte LDS read of 16 fp8).
-  bf16x8_t qf[18];
-  {
-    const uint16_t* qrow = a.q + (int64_t)row_out * kRowDim;
+  bf16x8_t qf[HT][18];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const uint16_t* qrow = a.q + (int64_t)row_out[ht] * kRowDim;
 #pragma unroll
     for (int t = 0; t < 18; ++t) {
       const int d = FP8 ? (64 * (t >> 1) + 16 * g4 + 8 * (t & 1)) : (32 * t + 8 * g4);
       u32x4_t v = *(const u32x4_t*)(qrow + d);
-      if (!row_ok) v = u32x4_t{0, 0, 0, 0};
-      qf[t] = __builtin_bit_cast(bf16x8_t, v);
+      if (!row_ok[ht]) v = u32x4_t{0, 0, 0, 0};
+      qf[ht][t] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
 
   // ---- softmax state and output accumulators (O^T tiles: 16 latent cols x 16 heads)
-  float m_ref = -__builtin_inff(), l_part = 0.0f;
-  f32x4_t o_acc[32];
+  float m_ref[HT], l_part[HT];
+  f32x4_t o_acc[32][HT];
 #pragma unroll
-  for (int nt = 0; nt < 32; ++nt) o_acc[nt] = f32x4_t{0, 0, 0, 0};
+  for (int ht = 0; ht < HT; ++ht) {
+    m_ref[ht] = -__builtin_inff();
+    l_part[ht] = 0.0f;
+#pragma unroll
+    for (int nt = 0; nt < 32; ++nt) o_acc[nt][ht] = f32x4_t{0, 0, 0, 0};
+  }
 
   // ---- page-gathered block loads. global_load_lds puts lane i of an
   // instruction at LDS base + 16*i; the lane picks which 16-byte piece of
@@ -268,17 +294,31 @@ void mla_decode_kernel(DecodeArgs a) {
   constexpr int RPW = Cfg::kRowsPerWave;
   // Page ids are fetched one block ahead of their use, so that reading them
   // never waits on the cache rows in flight; validation happens at use.
-  auto row_kv = [&](int blk) -> int {  // cache row of this lane (lanes < RPW) in block blk
-    const int kv = c_start + blk * kBlockRows + wave * RPW + lane;
-    return min(kv, c_end - 1);  // rows past the chunk repeat its last row; they are masked
+  // Lane l < RPW follows cache row c_start + 64*blk + wave*RPW + l; rows past
+  // the chunk end repeat its last row, whose scores are masked. Division by
+  // the page size uses a float reciprocal plus one correction step (exact for
+  // row indices below 2^24; context lengths are int32 and far below that).
+  const float rcp_p = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, 1.0f / (float)P)));
+  auto fetch_page = [&](int blk, int& off) -> int {
+    const int kv = min(c_start + blk * kBlockRows + wave * RPW + lane, c_end - 1);
+    int q = (int)((float)kv * rcp_p);
+    int r = kv - q * P;
+    if (r < 0) {
+      --q;
+      r += P;
+    } else if (r >= P) {
+      ++q;
+      r -= P;
+    }
+    off = r;
+    return a.kv_page_indices[page_base + q];
   };
-  auto fetch_page = [&](int blk) -> int { return a.kv_page_indices[page_base + row_kv(blk) / P]; };
-  auto page_slot = [&](int blk, int page) -> int {
+  auto page_slot = [&](int page, int off) -> int {
     if ((uint64_t)(int64_t)page >= (uint64_t)a.num_pages) {
       atomicOr(a.status, MLA_DEV_PAGE_OUT_OF_RANGE);
       page = 0;
     }
-    return page * P + row_kv(blk) % P;
+    return page * P + off;
   };
   auto issue_block = [&](int blk, int slot_reg) {
     const uint32_t stage_off = (uint32_t)(blk & 1) * L::kBlockBytes;
@@ -287,19 +327,22 @@ void mla_decode_kernel(DecodeArgs a) {
     // (bf16: 64 slots; fp8: 32 slots, upper half of the wave idle)
 #pragma unroll
     for (int rl = 0; rl < RPW; ++rl) {
-      const int slot = __builtin_amdgcn_readlane(slot_reg, rl);
-      const uint8_t* src = cache + (int64_t)slot * L::kRowBytes + (lane << 4);
+      // the row base is uniform: form it in scalar registers, then add the lane's slot
+      const uint64_t rowp = (uint64_t)(uintptr_t)cache + (uint64_t)(uint32_t)__builtin_amdgcn_readlane(slot_reg, rl) * L::kRowBytes;
+      const uint32_t rlo = __builtin_amdgcn_readfirstlane((uint32_t)rowp);
+      const uint32_t rhi = __builtin_amdgcn_readfirstlane((uint32_t)(rowp >> 32));
+      const uint8_t* src = (const uint8_t*)(((uint64_t)rhi << 32 | rlo) + (uint32_t)(lane << 4));
       const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_base + stage_off + (uint32_t)((r_base + rl) * L::kMainStride));
       if (FP8 ? lane < 32 : true) dma16(src, dst);
     }
     // tail: kTailRowsPerInst rows x kTailSlots slots per instruction
     const int tslot = lane % L::kTailSlots;
     const int trow = lane / L::kTailSlots;
-    const int logical = tslot ^ (trow % L::kTailSlots);  // r % kTailSlots == trow % kTailSlots
 #pragma unroll
     for (int m = 0; m < Cfg::kTailInsts; ++m) {
       const int rl = m * Cfg::kTailRowsPerInst + trow;
       const int slot = __shfl(slot_reg, rl & 63);
+      const int logical = tslot ^ L::tail_xor(r_base + rl);
       const uint8_t* src = cache + (int64_t)slot * L::kRowBytes + L::kMainBytes + (logical << 4);
       const uint32_t dst = __builtin_amdgcn_readfirstlane(
           lds_base + stage_off + (uint32_t)(L::kTailBase + (r_base + m * Cfg::kTailRowsPerInst) * L::kTailBytes));
@@ -308,25 +351,30 @@ void mla_decode_kernel(DecodeArgs a) {
   };
 
   // Per-lane LDS offsets that do not change over the loop; each access adds a
-  // compile-time immediate.
-  const int pi16 = (i16 >> 2) + 4 * (i16 & 3);  // LDS row read by MFMA row i16 of a K tile
-  const uint32_t k_main_base = (uint32_t)pi16 * L::kMainStride + (uint32_t)g4 * 16;
-  const uint32_t k_tail_row = L::kTailBase + (uint32_t)pi16 * L::kTailBytes;
-  uint32_t v_base;
+  // compile-time immediate. Index [o] is for tiles with nt & 1 == o.
+  uint32_t k_main_base[2];
+#pragma unroll
+  for (int o = 0; o < 2; ++o) k_main_base[o] = (uint32_t)perm_row(i16, o) * L::kMainStride + (uint32_t)g4 * 16;
+  // V^T reads of P^T fragment u: element e < 4 is kv row 32u + pi_0(4g4 + e),
+  // e >= 4 is 32u + 16 + pi_1(4g4 + e - 4).
+  uint32_t v_base_lo, v_base_hi;
   if constexpr (FP8) {
-    // supplier lane (k = i16/2, c = i16%2): row g4 + 4(k&3) + 16(k>>2), bytes 8c of the column tile
+    // supplier lane (k = i16/2, c = i16%2) reads element k's row, bytes 8c of the column tile
     const int k = i16 >> 1, c = i16 & 1;
-    v_base = (uint32_t)(g4 + 4 * (k & 3) + 16 * (k >> 2)) * L::kMainStride + 8u * c;
+    const int row = k < 4 ? perm_row(4 * g4 + k, 0) : 16 + perm_row(4 * g4 + k - 4, 1);
+    v_base_lo = (uint32_t)row * L::kMainStride + 8u * c;
+    v_base_hi = v_base_lo;
   } else {
-    // supplier lane (k = i16/4, c = i16%4): row g4 + 4k (and +16), elements 4c of the column tile
+    // supplier lane (k = i16/4, c = i16%4) reads rows of elements k and 4+k, columns 4c..4c+3
     const int k = i16 >> 2, c = i16 & 3;
-    v_base = (uint32_t)(g4 + 4 * k) * L::kMainStride + 8u * c;
+    v_base_lo = (uint32_t)perm_row(4 * g4 + k, 0) * L::kMainStride + 8u * c;
+    v_base_hi = (uint32_t)(16 + perm_row(4 * g4 + k, 1)) * L::kMainStride + 8u * c;
   }
 
-  int page_next = 0;
-  if (lane < RPW) page_next = fetch_page(0);
-  issue_block(0, lane < RPW ? page_slot(0, page_next) : 0);
-  if (nblk > 1 && lane < RPW) page_next = fetch_page(1);
+  int page_next = 0, off_next = 0;
+  if (lane < RPW) page_next = fetch_page(0, off_next);
+  issue_block(0, lane < RPW ? page_slot(page_next, off_next) : 0);
+  if (nblk > 1 && lane < RPW) page_next = fetch_page(1, off_next);
 
   const float sscale = a.score_scale_log2;
 
@@ -334,34 +382,36 @@ void mla_decode_kernel(DecodeArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (blk + 1 < nblk) {
-      issue_block(blk + 1, lane < RPW ? page_slot(blk + 1, page_next) : 0);
-      if (blk + 2 < nblk && lane < RPW) page_next = fetch_page(blk + 2);
+      issue_block(blk + 1, lane < RPW ? page_slot(page_next, off_next) : 0);
+      if (blk + 2 < nblk && lane < RPW) page_next = fetch_page(blk + 2, off_next);
     }
     LDS_PTR(uint8_t) stage = lds + (uint32_t)(blk & 1) * L::kBlockBytes;
     const int kv0 = c_start + blk * kBlockRows;
 
     // ---- S^T[kv, head] = K Q^T for the 64 rows of the block (4 tiles of 16 kv rows).
     // The reads walk (step, tile) with a ring of KD reads in flight; every
-    // step ends in a scheduling barrier so the compiler cannot hoist the whole
-    // block's reads (which would exhaust the registers).
-    f32x4_t sacc[4];
+    // read is followed by a scheduling barrier so that the compiler cannot
+    // hoist the whole block's reads (which would exhaust the registers).
+    f32x4_t sacc[4][HT];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) sacc[nt] = f32x4_t{0, 0, 0, 0};
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) sacc[nt][ht] = f32x4_t{0, 0, 0, 0};
     {
       constexpr int kSteps = FP8 ? 9 : 18;
       constexpr int kMainSteps = FP8 ? 8 : 16;  // steps whose slots lie in the main region
       constexpr int kReads = kSteps * 4;
-      constexpr int KD = 3;
+      constexpr int KD = WPE == 2 ? 2 : (HT == 2 ? 3 : 8);
       u32x4_t kb[KD];
       auto kread = [&](int i) -> u32x4_t {
-        const int step = i >> 2, nt = i & 3;
+        const int step = i >> 2, nt = i & 3, o = nt & 1;
         uint32_t off;
         if (step < kMainSteps) {
-          off = k_main_base + (uint32_t)(nt * 16 * L::kMainStride + step * 64);
+          off = k_main_base[o] + (uint32_t)(nt * 16 * L::kMainStride + step * 64);
         } else {
           const int s2 = 4 * (step - kMainSteps) + g4;  // logical tail slot of this lane
-          off = k_tail_row + (uint32_t)(nt * 16 * L::kTailBytes) +
-                ((uint32_t)(s2 ^ (pi16 % L::kTailSlots)) << 4);
+          const int pr = perm_row(i16, o);
+          off = L::kTailBase + (uint32_t)((nt * 16 + pr) * L::kTailBytes) + ((uint32_t)(s2 ^ L::tail_xor(pr)) << 4);
         }
         return lds_b128(stage, off);
       };
@@ -374,83 +424,97 @@ void mla_decode_kernel(DecodeArgs a) {
         const int step = i >> 2, nt = i & 3;
         if constexpr (FP8) {
           // 16 fp8 = d in [64 step + 16 g4, +16): two k-steps of 8
-          sacc[nt] = mfma16(fp8x8_to_bf16x8(raw[0], raw[1]), qf[2 * step], sacc[nt]);
-          sacc[nt] = mfma16(fp8x8_to_bf16x8(raw[2], raw[3]), qf[2 * step + 1], sacc[nt]);
+          const bf16x8_t k0 = fp8x8_to_bf16x8(raw[0], raw[1]);
+          const bf16x8_t k1 = fp8x8_to_bf16x8(raw[2], raw[3]);
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) {
+            sacc[nt][ht] = mfma16(k0, qf[ht][2 * step], sacc[nt][ht]);
+            sacc[nt][ht] = mfma16(k1, qf[ht][2 * step + 1], sacc[nt][ht]);
+          }
         } else {
-          sacc[nt] = mfma16(__builtin_bit_cast(bf16x8_t, raw), qf[step], sacc[nt]);
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) sacc[nt][ht] = mfma16(__builtin_bit_cast(bf16x8_t, raw), qf[ht][step], sacc[nt][ht]);
         }
-        __builtin_amdgcn_sched_barrier(0);
+        MLA_STEP_BARRIER();
       }
     }
 
-    // ---- mask, online softmax (lane = one head row, 16 kv values per lane)
-    bf16x8_t pf[2];
-    float alpha;
-    bool up;
-    {
+    // ---- mask, online softmax (lane = one head row per tile, 16 kv values per lane)
+    bf16x8_t pf[HT][2];
+    float alpha[HT];
+    bool any_up = false;
+    // score row 4g4+r of tile nt is cache row kv0 + nt*16 + 2r + (pg ^ (nt&1)),
+    // pg = 8(g4&1) + (g4>>1); compare the compile-time part against a limit.
+    const int pg = 8 * (g4 & 1) + (g4 >> 1);
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const int lim0 = vis_end[ht] - kv0 - pg, lim1 = vis_end[ht] - kv0 - (pg ^ 1);
       float mx = -__builtin_inff();
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int kv = kv0 + nt * 16 + g4 + 4 * r;  // score row 4g4+r of tile nt
-          float v = sacc[nt][r] * sscale;
-          v = kv < vis_end ? v : -__builtin_inff();
-          sacc[nt][r] = v;
+          float v = sacc[nt][ht][r] * sscale;
+          v = nt * 16 + 2 * r < ((nt & 1) ? lim1 : lim0) ? v : -__builtin_inff();
+          sacc[nt][ht][r] = v;
           mx = fmaxf(mx, v);
         }
       mx = wave_max_16x4(mx);
-      const float old = m_ref;
-      up = mx > old + kRescaleSlack;
+      const float old = m_ref[ht];
+      const bool up = mx > old + kRescaleSlack;
       const float m_new = up ? mx : old;
-      alpha = up ? exp2f(old - m_new) : 1.0f;  // old = -inf gives 0
-      m_ref = m_new;
+      alpha[ht] = up ? __builtin_amdgcn_exp2f(old - m_new) : 1.0f;  // old = -inf gives 0
+      any_up |= up;
+      m_ref[ht] = m_new;
       const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;
       float psum = 0.0f;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = exp2f(sacc[nt][r] - m_use);
-          sacc[nt][r] = p;
+          const float p = __builtin_amdgcn_exp2f(sacc[nt][ht][r] - m_use);
+          sacc[nt][ht][r] = p;
           psum += p;
         }
-      l_part = l_part * alpha + psum;
+      l_part[ht] = l_part[ht] * alpha[ht] + psum;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         u32x4_t w;
-        w[0] = pack_bf16x2(sacc[2 * u][0], sacc[2 * u][1]);
-        w[1] = pack_bf16x2(sacc[2 * u][2], sacc[2 * u][3]);
-        w[2] = pack_bf16x2(sacc[2 * u + 1][0], sacc[2 * u + 1][1]);
-        w[3] = pack_bf16x2(sacc[2 * u + 1][2], sacc[2 * u + 1][3]);
-        pf[u] = __builtin_bit_cast(bf16x8_t, w);
+        w[0] = pack_bf16x2(sacc[2 * u][ht][0], sacc[2 * u][ht][1]);
+        w[1] = pack_bf16x2(sacc[2 * u][ht][2], sacc[2 * u][ht][3]);
+        w[2] = pack_bf16x2(sacc[2 * u + 1][ht][0], sacc[2 * u + 1][ht][1]);
+        w[3] = pack_bf16x2(sacc[2 * u + 1][ht][2], sacc[2 * u + 1][ht][3]);
+        pf[ht][u] = __builtin_bit_cast(bf16x8_t, w);
       }
     }
-    if (__builtin_amdgcn_ballot_w64(up)) {
+    if (__builtin_amdgcn_ballot_w64(any_up)) {
 #pragma unroll
-      for (int nt = 0; nt < 32; ++nt) o_acc[nt] *= alpha;
+      for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int nt = 0; nt < 32; ++nt) o_acc[nt][ht] *= alpha[ht];
     }
 
     // ---- O^T[n, head] += V^T P^T ; V^T fragments by transposed LDS reads.
-    // P^T fragment u, lane (head, g4) holds kv rows {32u + g4 + 4r, 32u + 16 + g4 + 4r}, r < 4;
-    // the V^T fragment must hold the same kv rows, in the same order, for its latent column.
+    // P^T fragment u, lane (head, g4) holds kv rows 32u + pi_0(4g4 + r) (r < 4)
+    // then 32u + 16 + pi_1(4g4 + r); the V^T fragment holds the same rows, in
+    // the same order, for its latent column.
     {
-      constexpr int VD = 4;  // V^T fragments in flight
+      constexpr int VD = WPE == 2 ? 2 : (HT == 2 ? 3 : 8);  // V^T fragments in flight
       u32x4_t vb[VD];
       auto vread = [&](int j) -> u32x4_t {
         const int u = j >> 5, nt = j & 31;
         u32x4_t w;
         if constexpr (FP8) {
-          const uint32_t off = v_base + (uint32_t)(32 * u * L::kMainStride + nt * 16);
+          const uint32_t off = v_base_lo + (uint32_t)(32 * u * L::kMainStride + nt * 16);
           const i32x2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(i32x2_t))(stage + off));
           w[0] = (unsigned)raw[0];
           w[1] = (unsigned)raw[1];
           w[2] = 0;
           w[3] = 0;
         } else {
-          const uint32_t off = v_base + (uint32_t)(32 * u * L::kMainStride + nt * 32);
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4_t))(stage + off));
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4_t))(stage + off + 16 * L::kMainStride));
+          const uint32_t imm = (uint32_t)(32 * u * L::kMainStride + nt * 32);
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4_t))(stage + v_base_lo + imm));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4_t))(stage + v_base_hi + imm));
           const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
           const u32x2_t h2 = __builtin_bit_cast(u32x2_t, hi);
           w[0] = l2[0];
@@ -467,46 +531,59 @@ void mla_decode_kernel(DecodeArgs a) {
         if (j + VD - 1 < 64) vb[(j + VD - 1) % VD] = vread(j + VD - 1);
         const u32x4_t w = vb[j % VD];
         const bf16x8_t vf = FP8 ? fp8x8_to_bf16x8(w[0], w[1]) : __builtin_bit_cast(bf16x8_t, w);
-        o_acc[j & 31] = mfma16(vf, pf[j >> 5], o_acc[j & 31]);
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) o_acc[j & 31][ht] = mfma16(vf, pf[ht][j >> 5], o_acc[j & 31][ht]);
+        MLA_STEP_BARRIER();
       }
     }
   }
 
   // ---- epilogue: normalise, then the final row (single chunk) or a partial record
-  const float l = wave_sum_16x4(l_part);
-  const bool empty = !(l > 0.0f);
-  const float inv = empty ? 0.0f : a.out_scale / l;
-  const float lse2 = empty ? -__builtin_inff() : m_ref + __log2f(l);
-  if (!row_ok) return;
-  if (n_b == 1) {
-    uint16_t* orow = a.out + (int64_t)row_out * kLatentDim;
 #pragma unroll
-    for (int nt = 0; nt < 32; ++nt) {
-      const f32x4_t o = o_acc[nt] * inv;
-      u32x2_t w;
-      w[0] = pack_bf16x2(o[0], o[1]);
-      w[1] = pack_bf16x2(o[2], o[3]);
-      *(u32x2_t*)(orow + nt * 16 + 4 * g4) = w;
+  for (int ht = 0; ht < HT; ++ht) {
+    const float l = wave_sum_16x4(l_part[ht]);
+    const bool empty = !(l > 0.0f);
+    const float inv = empty ? 0.0f : a.out_scale / l;
+    const float lse2 = empty ? -__builtin_inff() : m_ref[ht] + __log2f(l);
+    if (!row_ok[ht]) continue;
+    if (n_b == 1) {
+      uint16_t* orow = a.out + (int64_t)row_out[ht] * kLatentDim;
+#pragma unroll
+      for (int nt = 0; nt < 32; ++nt) {
+        const f32x4_t o = o_acc[nt][ht] * inv;
+        u32x2_t w;
+        w[0] = pack_bf16x2(o[0], o[1]);
+        w[1] = pack_bf16x2(o[2], o[3]);
+        *(u32x2_t*)(orow + nt * 16 + 4 * g4) = w;
+      }
+      if (a.lse && g4 == 0) a.lse[row_out[ht]] = lse2 * kLn2;
+    } else {
+      const int64_t rec = (int64_t)a.partbase[b] + (int64_t)grp * n_b + chunk;
+      float* prow = a.part_out + (rec * a.rows_per_group + row_rr[ht]) * kLatentDim;
+#pragma unroll
+      for (int nt = 0; nt < 32; ++nt) *(f32x4_t*)(prow + nt * 16 + 4 * g4) = o_acc[nt][ht] * inv;
+      if (g4 == 0) a.part_lse[rec * a.rows_per_group + row_rr[ht]] = lse2;
     }
-    if (a.lse && g4 == 0) a.lse[row_out] = lse2 * kLn2;
-  } else {
-    const int64_t rec = (int64_t)a.partbase[b] + (int64_t)grp * n_b + chunk;
-    float* prow = a.part_out + (rec * a.rows_per_group + rr) * kLatentDim;
-#pragma unroll
-    for (int nt = 0; nt < 32; ++nt) *(f32x4_t*)(prow + nt * 16 + 4 * g4) = o_acc[nt] * inv;
-    if (g4 == 0) a.part_lse[rec * a.rows_per_group + rr] = lse2;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Combine: one workgroup (4 waves) per (column block, tile row, sequence x group).
-// Wave w merges chunks w, w+4, ...; the four partial states meet in LDS.
-template <int CPL>  // columns per lane: 8 (512-column blocks) or 1 (64-column blocks)
+// Combine: one workgroup (256 threads) per (column block of CB columns, tile
+// row, sequence x group). Phase 1 turns every partial lse into a weight
+// 2^(lse_c - M) in LDS; phase 2 has 1024/CB streams of threads, each thread
+// owning 4 columns, accumulate the weighted partial outputs of chunks
+// stream, stream + nstreams, ... with independent loads; phase 3 sums the
+// streams. CB shrinks when there are few rows to merge, so that many
+// workgroups share a long list of chunks.
+constexpr int kCombineMaxChunks = 2048;  // chunks weighed per pass of phase 1
+
+template <int CB>
 __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
-  constexpr int kCols = CPL * 64;
-  __shared__ float st_m[4], st_s[4];
-  __shared__ float st_acc[4][kCols];
+  constexpr int kThreadsPerChunk = CB / 4;
+  constexpr int kStreams = 256 / kThreadsPerChunk;
+  __shared__ float w_lds[kCombineMaxChunks];
+  __shared__ float red[256];
+  __shared__ __attribute__((aligned(16))) float acc_lds[kStreams][CB];
   const int colblk = blockIdx.x;
   const int rr = blockIdx.y;
   const int b = blockIdx.z / a.num_groups;
@@ -516,59 +593,79 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
   const int s = rr / a.heads_per_group;
   const int head = grp * a.heads_per_group + rr % a.heads_per_group;
   if (head >= a.num_heads) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col0 = colblk * kCols + lane * CPL;
+  const int tid = threadIdx.x;
   const int64_t rec0 = (int64_t)a.partbase[b] + (int64_t)grp * n_b;
+  const int nw = min(n_b, kCombineMaxChunks);
 
-  float m = -__builtin_inff(), ssum = 0.0f, acc[CPL];
-  for (int j = 0; j < CPL; ++j) acc[j] = 0.0f;
-  for (int c = wave; c < n_b; c += 4) {
-    const int64_t idx = (rec0 + c) * a.rows_per_group + rr;
-    const float l = a.part_lse[idx];
-    if (l == -__builtin_inff()) continue;
-    const float m_new = fmaxf(m, l);
-    const float f_old = exp2f(m - m_new);
-    const float f_c = exp2f(l - m_new);
-    const float* src = a.part_out + idx * kLatentDim + col0;
-    ssum = ssum * f_old + f_c;
-    if constexpr (CPL == 8) {
-      const f32x4_t x0 = *(const f32x4_t*)(src);
-      const f32x4_t x1 = *(const f32x4_t*)(src + 4);
-      for (int j = 0; j < 4; ++j) {
-        acc[j] = acc[j] * f_old + f_c * x0[j];
-        acc[4 + j] = acc[4 + j] * f_old + f_c * x1[j];
-      }
-    } else {
-      for (int j = 0; j < CPL; ++j) acc[j] = acc[j] * f_old + f_c * src[j];
-    }
-    m = m_new;
-  }
-  if (lane == 0) {
-    st_m[wave] = m;
-    st_s[wave] = ssum;
-  }
-  for (int j = 0; j < CPL; ++j) st_acc[wave][lane * CPL + j] = acc[j];
+  // ---- phase 1: weights. A chunk with no visible row has lse = -inf (weight 0).
+  float m = -__builtin_inff();
+  for (int c = tid; c < n_b; c += 256) m = fmaxf(m, a.part_lse[(rec0 + c) * a.rows_per_group + rr]);
+  red[tid] = m;
   __syncthreads();
-  float M = fmaxf(fmaxf(st_m[0], st_m[1]), fmaxf(st_m[2], st_m[3]));
-  const bool empty = M == -__builtin_inff();
-  float f[4], total = 0.0f;
-  for (int w = 0; w < 4; ++w) {
-    f[w] = empty ? 0.0f : exp2f(st_m[w] - M);
-    total += f[w] * st_s[w];
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
+    __syncthreads();
   }
+  const float M = red[0];
+  const bool empty = M == -__builtin_inff();
+  __syncthreads();
+  float wsum = 0.0f;
+  for (int c = tid; c < n_b; c += 256) {
+    const float w = empty ? 0.0f : __builtin_amdgcn_exp2f(a.part_lse[(rec0 + c) * a.rows_per_group + rr] - M);
+    wsum += w;
+    if (c < nw) w_lds[c] = w;
+  }
+  red[tid] = wsum;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) red[tid] += red[tid + off];
+    __syncthreads();
+  }
+  const float total = red[0];
+
+  // ---- phase 2: weighted sum of the partial outputs
+  const int stream = tid / kThreadsPerChunk;
+  const int col = colblk * CB + (tid % kThreadsPerChunk) * 4;
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  const float* base = a.part_out + (rec0 * a.rows_per_group + rr) * kLatentDim + col;
+  const int64_t rec_stride = (int64_t)a.rows_per_group * kLatentDim;
+  for (int c0 = 0; c0 < n_b; c0 += kCombineMaxChunks) {
+    if (c0 > 0) {  // weights of the next pass
+      __syncthreads();
+      for (int c = c0 + tid; c < min(n_b, c0 + kCombineMaxChunks); c += 256)
+        w_lds[c - c0] = empty ? 0.0f : __builtin_amdgcn_exp2f(a.part_lse[(rec0 + c) * a.rows_per_group + rr] - M);
+      __syncthreads();
+    }
+    const int cend = min(n_b, c0 + kCombineMaxChunks);
+    int c = c0 + stream;
+    for (; c + 3 * kStreams < cend; c += 4 * kStreams) {
+      f32x4_t x[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[k] = *(const f32x4_t*)(base + (int64_t)(c + k * kStreams) * rec_stride);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc += w_lds[c + k * kStreams - c0] * x[k];
+    }
+    for (; c < cend; c += kStreams) acc += w_lds[c - c0] * *(const f32x4_t*)(base + (int64_t)c * rec_stride);
+  }
+
+  // ---- phase 3: sum the streams, normalise, store
+  *(f32x4_t*)&acc_lds[stream][(tid % kThreadsPerChunk) * 4] = acc;
+  __syncthreads();
   const float inv = total > 0.0f ? 1.0f / total : 0.0f;
   const int64_t orow = ((int64_t)b * a.seqlen_qo + s) * a.num_heads + head;
-  for (int c = threadIdx.x; c < kCols; c += 256) {
-    const float v = (f[0] * st_acc[0][c] + f[1] * st_acc[1][c] + f[2] * st_acc[2][c] + f[3] * st_acc[3][c]) * inv;
-    a.out[orow * kLatentDim + colblk * kCols + c] = __builtin_bit_cast(uint16_t, (__bf16)v);
+  for (int cc = tid; cc < CB; cc += 256) {
+    float v = 0.0f;
+#pragma unroll 8
+    for (int st = 0; st < kStreams; ++st) v += acc_lds[st][cc];
+    a.out[orow * kLatentDim + colblk * CB + cc] = __builtin_bit_cast(uint16_t, (__bf16)(v * inv));
   }
-  if (a.lse && colblk == 0 && threadIdx.x == 0)
+  if (a.lse && colblk == 0 && tid == 0)
     a.lse[orow] = empty ? -__builtin_inff() : (M + __log2f(total)) * kLn2;
 }
 
-template <bool FP8, int NW>
+template <bool FP8, int NW, int HT, int WPE>
 int launch_decode_t(const DecodeArgs& a, int gx, int gy, int gz, hipStream_t st) {
-  hipLaunchKernelGGL((mla_decode_kernel<FP8, NW>), dim3(gx, gy, gz), dim3(NW * 64), 0, st, a);
+  hipLaunchKernelGGL((mla_decode_kernel<FP8, NW, HT, WPE>), dim3(gx, gy, gz), dim3(NW * 64), 0, st, a);
   return (int)hipGetLastError();
 }
 
@@ -579,15 +676,17 @@ int launch_plan(const PlanArgs& a, void* stream) {
   return (int)hipGetLastError();
 }
 
-// Tile classes: 16, 32, 64, 128 rows -> 1, 2, 4, 8 waves of one 16-row head tile each.
+// Tile classes: 16, 32, 64, 128 rows -> 1, 2, 4, 8 waves of one 16-row head
+// tile. The 128-row tile runs two waves per SIMD (256 registers each); the
+// smaller tiles one wave per SIMD per workgroup.
 int launch_decode(const DecodeArgs& a, int kv_dtype, int tile_class, int gx, int gy, int gz, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const bool fp8 = kv_dtype == MLA_KV_FP8_E4M3FN;
   switch (tile_class) {
-    case 0: return fp8 ? launch_decode_t<true, 1>(a, gx, gy, gz, st) : launch_decode_t<false, 1>(a, gx, gy, gz, st);
-    case 1: return fp8 ? launch_decode_t<true, 2>(a, gx, gy, gz, st) : launch_decode_t<false, 2>(a, gx, gy, gz, st);
-    case 2: return fp8 ? launch_decode_t<true, 4>(a, gx, gy, gz, st) : launch_decode_t<false, 4>(a, gx, gy, gz, st);
-    case 3: return fp8 ? launch_decode_t<true, 8>(a, gx, gy, gz, st) : launch_decode_t<false, 8>(a, gx, gy, gz, st);
+    case 0: return fp8 ? launch_decode_t<true, 1, 1, 1>(a, gx, gy, gz, st) : launch_decode_t<false, 1, 1, 1>(a, gx, gy, gz, st);
+    case 1: return fp8 ? launch_decode_t<true, 2, 1, 1>(a, gx, gy, gz, st) : launch_decode_t<false, 2, 1, 1>(a, gx, gy, gz, st);
+    case 2: return fp8 ? launch_decode_t<true, 4, 1, 1>(a, gx, gy, gz, st) : launch_decode_t<false, 4, 1, 1>(a, gx, gy, gz, st);
+    case 3: return fp8 ? launch_decode_t<true, 8, 1, 2>(a, gx, gy, gz, st) : launch_decode_t<false, 8, 1, 2>(a, gx, gy, gz, st);
   }
   return (int)hipErrorInvalidValue;
 }
@@ -596,10 +695,14 @@ int launch_combine(const CombineArgs& a, int max_chunks, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const int rows = a.rows_per_group;
   const int gz = a.batch * a.num_groups;
-  if (max_chunks <= 16) {
-    hipLaunchKernelGGL(mla_combine_kernel<8>, dim3(1, rows, gz), dim3(256), 0, st, a);
+  // Narrow column blocks when few rows carry long chunk lists.
+  const int64_t row_count = (int64_t)gz * rows;
+  if (row_count >= 1024 || max_chunks <= 8) {
+    hipLaunchKernelGGL(mla_combine_kernel<512>, dim3(1, rows, gz), dim3(256), 0, st, a);
+  } else if (row_count >= 128) {
+    hipLaunchKernelGGL(mla_combine_kernel<128>, dim3(kLatentDim / 128, rows, gz), dim3(256), 0, st, a);
   } else {
-    hipLaunchKernelGGL(mla_combine_kernel<1>, dim3(kLatentDim / 64, rows, gz), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(mla_combine_kernel<16>, dim3(kLatentDim / 16, rows, gz), dim3(256), 0, st, a);
   }
   return (int)hipGetLastError();
 }
