@@ -3,10 +3,11 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 One step = one call of the hot path (mla_decode + mla_split_combine) over the
-whole batch, inputs resident in HBM. Between steps a 1 GiB buffer is
-overwritten (outside the timed events) so that neither L2 nor the 256 MB MALL
-holds the previous call's cache rows, as in serving where other layers run in
-between. Prints one JSON line.
+whole batch, inputs resident in HBM. Between steps a 1 GiB buffer is read
+(outside the timed events) so that neither L2 nor the 256 MB MALL holds the
+previous call's cache rows, as in serving where other layers run in between.
+The flush reads rather than writes: a write leaves ~256 MB of dirty lines whose
+write-back would compete with the next call's reads. Prints one JSON line.
 
 Roofline accounting (per decode launch):
   algorithmic bytes = sum_b ctx_b * 576 * e (each cache row read once; e = 2 bf16, 1 fp8)
@@ -113,7 +114,7 @@ def main():
     dec = Decoder(inp, None, 0, stream)
     torch.cuda.synchronize()
     plan_us = (time.perf_counter() - t0) * 1e6
-    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush = None if args.no_flush else torch.ones(1 << 28, dtype=torch.float32, device="cuda")
 
     def step(ev=None):
         if ev is not None:
@@ -126,16 +127,17 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
     for _ in range(args.warmup):
         if flush is not None:
-            flush.fill_(1)
+            torch.sum(flush, dim=0, out=sink)
         step()
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     wall0 = time.perf_counter()
     for k in range(args.steps):
         if flush is not None:
-            flush.fill_(k & 0xFF)
+            torch.sum(flush, dim=0, out=sink)
         step(events[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0

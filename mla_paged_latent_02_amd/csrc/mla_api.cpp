@@ -66,6 +66,7 @@ mla_status_t mla_decode(const mla_plan_t* plan, const void* d_q, const void* d_k
   a.part_out = reinterpret_cast<float*>(ws_at(d_workspace, plan->ws_part_out_offset));
   a.part_lse = reinterpret_cast<float*>(ws_at(d_workspace, plan->ws_part_lse_offset));
   a.num_pages = p.num_slots / p.page_size;
+  a.page_div_magic = uint32_t(0xFFFFFFFFull / uint64_t(p.page_size));
   a.batch = p.batch;
   a.seqlen_qo = p.seqlen_qo;
   a.num_heads = p.num_heads;

@@ -28,6 +28,7 @@ struct DecodeArgs {
   float* part_out;              // [records][rows][512]
   float* part_lse;              // [records][rows]
   int64_t num_pages;            // num_slots / page_size
+  uint32_t page_div_magic;      // floor((2^32 - 1) / page_size): q = umulhi(n, magic), then one correction
   int32_t batch, seqlen_qo, num_heads, page_size;
   int32_t heads_per_group, num_groups, rows_per_group, chunk_len;
   int32_t causal;

@@ -140,22 +140,23 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(PlanArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode. One workgroup = one (chunk, head group, sequence). NW waves; wave w
-// owns tile rows [w*HT*16, (w+1)*HT*16) and all 64 cache rows of each block.
+// Decode. One workgroup = one (chunk, head group, sequence); NW waves, each
+// owning one 16-row head tile (its query fragments and its 16 x 512 fp32
+// output stay in registers for the whole chunk); all waves share each block
+// of BN cache rows in LDS. NS blocks are in flight in an LDS ring.
 //
-// LDS block layout (one pipeline stage, 64 cache rows):
+// LDS block layout (one stage, BN cache rows):
 //   main region: row r at r*kMainStride holds the 512 latent elements (the V
 //                part); the stride is padded by 16 bytes so that consecutive
 //                rows start on different banks;
 //   tail region: row r at kTailBase + r*kTailBytes holds the 64 rope elements
 //                (16-byte slots, physical slot p holds logical slot
-//                p ^ (r % kTailSlots)).
+//                p ^ tail_xor(r)).
 // Row permutations: MFMA row m = 4g + r (g = m/4) of K tile nt reads LDS row
 // nt*16 + pi_{nt&1}(m), pi_0(m) = 2r + 8(g&1) + (g>>1), pi_1(m) = pi_0(m) ^ 1.
 // So each 32-lane half of a transposed V read (tiles 2u, 2u+1) touches rows
-// that fall in distinct bank groups, and a K read touches 16 distinct rows.
-// Tail slots are swizzled with the row bits above the bank-group bit(s).
-template <bool FP8>
+// in distinct bank groups, and a K read touches 16 distinct rows.
+template <bool FP8, int BN>
 struct RowLayout {
   static constexpr int kElem = FP8 ? 1 : 2;
   static constexpr int kRowBytes = kRowDim * kElem;      // 576 or 1152 in the cache
@@ -163,24 +164,25 @@ struct RowLayout {
   static constexpr int kMainStride = kMainBytes + 16;
   static constexpr int kTailBytes = 64 * kElem;          // 64 or 128
   static constexpr int kTailSlots = kTailBytes / 16;     // 4 or 8
-  static constexpr int kTailBase = kBlockRows * kMainStride;
-  static constexpr int kBlockBytes = kTailBase + kBlockRows * kTailBytes;
-  // physical tail slot p of row r holds logical slot p ^ tail_xor(r): the tail
-  // row stride spans kTailBytes/4 banks, so the row bits above that pick the xor
-  static __device__ __forceinline__ int tail_xor(int r) {
-    return FP8 ? ((r >> 2) & 3) : ((r >> 1) & 7);
-  }
+  static constexpr int kTailBase = BN * kMainStride;
+  static constexpr int kBlockBytes = kTailBase + BN * kTailBytes;
+  // the tail row stride spans kTailBytes/4 banks; the row bits above that pick the xor
+  static __device__ __forceinline__ int tail_xor(int r) { return FP8 ? ((r >> 2) & 3) : ((r >> 1) & 7); }
 };
 
-template <bool FP8, int NW>
+template <bool FP8, int NW, int BN, int NS>
 struct DecodeCfg {
-  using L = RowLayout<FP8>;
-  static constexpr int kStages = 2;
-  static constexpr int kLdsBytes = kStages * L::kBlockBytes;
-  static constexpr int kRowsPerWave = kBlockRows / NW;  // rows each wave loads
+  using L = RowLayout<FP8, BN>;
+  static constexpr int kLdsBytes = NS * L::kBlockBytes;
+  static constexpr int kRowsPerWave = BN / NW;  // rows each wave gathers per block
   static constexpr int kTailRowsPerInst = 64 / L::kTailSlots;
   static constexpr int kTailInsts = (kRowsPerWave + kTailRowsPerInst - 1) / kTailRowsPerInst;
+  static constexpr int kDmaInsts = kRowsPerWave + kTailInsts;  // vector-memory instructions per wave per block
+  static constexpr int kTiles = BN / 16;                       // score tiles per block
+  static constexpr int kKSteps = BN / 32;                      // PV k-steps per block
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+  static_assert(kRowsPerWave >= 1 && BN % 32 == 0, "row split");
+  static_assert((NS - 2) * kDmaInsts <= 63, "vmcnt range");
 };
 
 __device__ __forceinline__ u32x4_t lds_b128(LDS_PTR(uint8_t) base, uint32_t off) {
@@ -190,10 +192,31 @@ __device__ __forceinline__ u32x4_t lds_b128(LDS_PTR(uint8_t) base, uint32_t off)
 // 16 bytes per lane from global memory straight into LDS at lds_addr + 16*lane
 // (global_load_lds_dwordx4; M0 holds the wave's LDS base). Written as inline
 // asm so that the compiler does not guard every later LDS read with a wait
-// for it: completion is awaited explicitly with s_waitcnt vmcnt(0) before the
-// workgroup barrier that publishes a stage.
+// for it: completion is awaited explicitly (vmcnt) before the workgroup
+// barrier that publishes a stage.
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory");
+}
+
+// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Wait until at most min(k, MAXK) * K DMA instructions of this wave are pending.
+template <int K, int MAXK>
+__device__ __forceinline__ void wait_vmcnt_blocks(int k) {
+  if constexpr (MAXK >= 1) {
+    if (k >= MAXK) {
+      wait_vmcnt<MAXK * K>();
+      return;
+    }
+    wait_vmcnt_blocks<K, MAXK - 1>(k);
+  } else {
+    wait_vmcnt<0>();
+  }
 }
 
 __device__ __forceinline__ int perm_row(int m, int odd) {
@@ -201,15 +224,14 @@ __device__ __forceinline__ int perm_row(int m, int odd) {
   return (2 * r + 8 * (g & 1) + (g >> 1)) ^ odd;
 }
 
-// One wave = HT head tiles of 16 rows: their query fragments (72 registers
-// per tile) and their 16 x 512 fp32 outputs (128 registers per tile) stay in
-// registers for the whole chunk. NW waves share each 64-row KV block in LDS;
-// one wave per SIMD (WPE = 1) leaves room for deep LDS prefetch.
-template <bool FP8, int NW, int HT, int WPE>
+template <bool FP8, int NW, int BN, int NS, int WPE, int KD, int VD>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void mla_decode_kernel(DecodeArgs a) {
-  using Cfg = DecodeCfg<FP8, NW>;
-  using L = RowLayout<FP8>;
+  using Cfg = DecodeCfg<FP8, NW, BN, NS>;
+  using L = typename Cfg::L;
+  constexpr int RPW = Cfg::kRowsPerWave;
+  constexpr int NT = Cfg::kTiles;
+  constexpr int NU = Cfg::kKSteps;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::kLdsBytes];
   LDS_PTR(uint8_t) lds = (LDS_PTR(uint8_t))smem;
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
@@ -242,97 +264,94 @@ void mla_decode_kernel(DecodeArgs a) {
   const int ctx = a.context_lens[b];
   const int c_start = chunk * a.chunk_len;
   const int c_end = min(c_start + a.chunk_len, ctx);
-  const int nblk = (c_end - c_start + kBlockRows - 1) / kBlockRows;
-  const int64_t page_base = a.kv_indptr[b];
+  const int nblk = (c_end - c_start + BN - 1) / BN;
+  const int page_base = a.kv_indptr[b];
   const int P = a.page_size;
 
-  // ---- this lane's tile rows (one per head tile) and their visible limits
-  int vis_end[HT], row_out[HT], row_rr[HT];
-  bool row_ok[HT];
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    const int rr = (wave * HT + ht) * 16 + i16;
+  // ---- this lane's tile row and its visible limit
+  int vis_end, row_out;
+  bool row_ok;
+  {
+    const int rr = wave * 16 + i16;
     const int tok = rr / a.heads_per_group;
     const int head = grp * a.heads_per_group + rr % a.heads_per_group;
-    row_rr[ht] = rr;
-    row_ok[ht] = rr < a.rows_per_group && head < a.num_heads;
-    vis_end[ht] = min(c_end, a.causal ? ctx - a.seqlen_qo + 1 + tok : ctx);
-    row_out[ht] = row_ok[ht] ? (int)(((int64_t)b * a.seqlen_qo + tok) * a.num_heads + head) : 0;
+    row_ok = rr < a.rows_per_group && head < a.num_heads;
+    vis_end = min(c_end, a.causal ? ctx - a.seqlen_qo + 1 + tok : ctx);
+    row_out = row_ok ? (int)(((int64_t)b * a.seqlen_qo + tok) * a.num_heads + head) : 0;
   }
 
   // ---- query fragments (B operand of S^T = K Q^T), resident for the whole chunk.
   // bf16 cache: fragment t holds d = 32t + 8*g4 .. +7.
   // fp8 cache:  fragment 2p+h holds d = 64p + 16*g4 + 8h .. +7 (one 16-byte LDS read of 16 fp8).
-  bf16x8_t qf[HT][18];
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    const uint16_t* qrow = a.q + (int64_t)row_out[ht] * kRowDim;
+  bf16x8_t qf[18];
+  {
+    const uint16_t* qrow = a.q + (int64_t)row_out * kRowDim;
 #pragma unroll
     for (int t = 0; t < 18; ++t) {
       const int d = FP8 ? (64 * (t >> 1) + 16 * g4 + 8 * (t & 1)) : (32 * t + 8 * g4);
       u32x4_t v = *(const u32x4_t*)(qrow + d);
-      if (!row_ok[ht]) v = u32x4_t{0, 0, 0, 0};
-      qf[ht][t] = __builtin_bit_cast(bf16x8_t, v);
+      if (!row_ok) v = u32x4_t{0, 0, 0, 0};
+      qf[t] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
 
   // ---- softmax state and output accumulators (O^T tiles: 16 latent cols x 16 heads)
-  float m_ref[HT], l_part[HT];
-  f32x4_t o_acc[32][HT];
+  float m_ref = -__builtin_inff(), l_part = 0.0f;
+  f32x4_t o_acc[32];
 #pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    m_ref[ht] = -__builtin_inff();
-    l_part[ht] = 0.0f;
-#pragma unroll
-    for (int nt = 0; nt < 32; ++nt) o_acc[nt][ht] = f32x4_t{0, 0, 0, 0};
-  }
+  for (int nt = 0; nt < 32; ++nt) o_acc[nt] = f32x4_t{0, 0, 0, 0};
 
-  // ---- page-gathered block loads. global_load_lds puts lane i of an
-  // instruction at LDS base + 16*i; the lane picks which 16-byte piece of
-  // which gathered row it fetches.
-  const uint8_t* cache = a.cache;
-  constexpr int RPW = Cfg::kRowsPerWave;
-  // Page ids are fetched one block ahead of their use, so that reading them
-  // never waits on the cache rows in flight; validation happens at use.
-  // Lane l < RPW follows cache row c_start + 64*blk + wave*RPW + l; rows past
-  // the chunk end repeat its last row, whose scores are masked. Division by
-  // the page size uses a float reciprocal plus one correction step (exact for
-  // row indices below 2^24; context lengths are int32 and far below that).
-  const float rcp_p = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, 1.0f / (float)P)));
-  auto fetch_page = [&](int blk, int& off) -> int {
-    const int kv = min(c_start + blk * kBlockRows + wave * RPW + lane, c_end - 1);
-    int q = (int)((float)kv * rcp_p);
-    int r = kv - q * P;
-    if (r < 0) {
-      --q;
-      r += P;
-    } else if (r >= P) {
+  // ---- page-gathered block loads.
+  // Page ids are read with scalar loads (wave-uniform addresses), so the only
+  // vector-memory instructions in the loop are the Cfg::kDmaInsts DMA
+  // instructions per block and the ring can wait for its oldest block alone.
+  // Row r of the wave's share of block blk is cache row
+  // min(c_start + blk*BN + wave*RPW + r, c_end - 1): rows past the chunk repeat
+  // its last row, whose scores are masked.
+  const __attribute__((address_space(4))) int32_t* page_ids =
+      (const __attribute__((address_space(4))) int32_t*)a.kv_page_indices;
+  const uint32_t magic = a.page_div_magic;
+  bool bad_page = false;
+  auto row_page_pos = [&](int blk, int r, int& q, int& rem) {
+    const int kv = __builtin_amdgcn_readfirstlane(min(c_start + blk * BN + wave * RPW + r, c_end - 1));
+    q = (int)__umulhi((uint32_t)kv, magic);
+    rem = kv - q * P;
+    if (rem >= P) {
       ++q;
-      r -= P;
+      rem -= P;
     }
-    off = r;
-    return a.kv_page_indices[page_base + q];
   };
-  auto page_slot = [&](int page, int off) -> int {
-    if ((uint64_t)(int64_t)page >= (uint64_t)a.num_pages) {
-      atomicOr(a.status, MLA_DEV_PAGE_OUT_OF_RANGE);
-      page = 0;
+  auto fetch_pages = [&](int blk, int (&page)[RPW]) {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      int q, rem;
+      row_page_pos(blk, r, q, rem);
+      page[r] = page_ids[page_base + q];
     }
-    return page * P + off;
   };
-  auto issue_block = [&](int blk, int slot_reg) {
-    const uint32_t stage_off = (uint32_t)(blk & 1) * L::kBlockBytes;
+  auto page_slots = [&](int blk, const int (&page)[RPW], int (&slot)[RPW]) {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      int q, rem;
+      row_page_pos(blk, r, q, rem);
+      int pg = page[r];
+      if ((uint32_t)pg >= (uint64_t)a.num_pages) {
+        bad_page = true;
+        pg = 0;
+      }
+      slot[r] = pg * P + rem;
+    }
+  };
+  const uint8_t* cache = a.cache;
+  auto issue_block = [&](int blk, const int (&slot)[RPW]) {
+    const uint32_t stage_off = (uint32_t)(blk % NS) * L::kBlockBytes;
     const int r_base = wave * RPW;
     // main: one instruction per row; lane l fetches the row's 16-byte slot l
     // (bf16: 64 slots; fp8: 32 slots, upper half of the wave idle)
 #pragma unroll
-    for (int rl = 0; rl < RPW; ++rl) {
-      // the row base is uniform: form it in scalar registers, then add the lane's slot
-      const uint64_t rowp = (uint64_t)(uintptr_t)cache + (uint64_t)(uint32_t)__builtin_amdgcn_readlane(slot_reg, rl) * L::kRowBytes;
-      const uint32_t rlo = __builtin_amdgcn_readfirstlane((uint32_t)rowp);
-      const uint32_t rhi = __builtin_amdgcn_readfirstlane((uint32_t)(rowp >> 32));
-      const uint8_t* src = (const uint8_t*)(((uint64_t)rhi << 32 | rlo) + (uint32_t)(lane << 4));
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_base + stage_off + (uint32_t)((r_base + rl) * L::kMainStride));
+    for (int r = 0; r < RPW; ++r) {
+      const uint8_t* src = cache + (int64_t)slot[r] * L::kRowBytes + (lane << 4);
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_base + stage_off + (uint32_t)((r_base + r) * L::kMainStride));
       if (FP8 ? lane < 32 : true) dma16(src, dst);
     }
     // tail: kTailRowsPerInst rows x kTailSlots slots per instruction
@@ -340,13 +359,16 @@ void mla_decode_kernel(DecodeArgs a) {
     const int trow = lane / L::kTailSlots;
 #pragma unroll
     for (int m = 0; m < Cfg::kTailInsts; ++m) {
-      const int rl = m * Cfg::kTailRowsPerInst + trow;
-      const int slot = __shfl(slot_reg, rl & 63);
-      const int logical = tslot ^ L::tail_xor(r_base + rl);
-      const uint8_t* src = cache + (int64_t)slot * L::kRowBytes + L::kMainBytes + (logical << 4);
+      int sv = slot[m * Cfg::kTailRowsPerInst];
+#pragma unroll
+      for (int k = 1; k < Cfg::kTailRowsPerInst; ++k)
+        if (m * Cfg::kTailRowsPerInst + k < RPW && trow == k) sv = slot[m * Cfg::kTailRowsPerInst + k];
+      const int r = r_base + m * Cfg::kTailRowsPerInst + trow;
+      const int logical = tslot ^ L::tail_xor(r);
+      const uint8_t* src = cache + (int64_t)sv * L::kRowBytes + L::kMainBytes + (logical << 4);
       const uint32_t dst = __builtin_amdgcn_readfirstlane(
           lds_base + stage_off + (uint32_t)(L::kTailBase + (r_base + m * Cfg::kTailRowsPerInst) * L::kTailBytes));
-      if (rl < RPW) dma16(src, dst);
+      if (m * Cfg::kTailRowsPerInst + trow < RPW) dma16(src, dst);
     }
   };
 
@@ -371,40 +393,45 @@ void mla_decode_kernel(DecodeArgs a) {
     v_base_hi = (uint32_t)(16 + perm_row(4 * g4 + k, 1)) * L::kMainStride + 8u * c;
   }
 
-  int page_next = 0, off_next = 0;
-  if (lane < RPW) page_next = fetch_page(0, off_next);
-  issue_block(0, lane < RPW ? page_slot(page_next, off_next) : 0);
-  if (nblk > 1 && lane < RPW) page_next = fetch_page(1, off_next);
+  // ---- prologue: blocks 0 .. NS-2 in flight, pages of block NS-1 fetched
+  int page_n[RPW], slot[RPW];
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i) {
+    if (i < nblk) {
+      fetch_pages(i, page_n);
+      page_slots(i, page_n, slot);
+      issue_block(i, slot);
+    }
+  }
+  if (NS - 1 < nblk) fetch_pages(NS - 1, page_n);
 
   const float sscale = a.score_scale_log2;
+  const int pg = 8 * (g4 & 1) + (g4 >> 1);  // score row 4g4+r of a tile is cache row 2r + (pg ^ (nt&1))
 
   for (int blk = 0; blk < nblk; ++blk) {
-    __builtin_amdgcn_s_waitcnt(0);
+    // blocks issued after this one so far: blk+1 .. min(blk+NS-2, nblk-1)
+    wait_vmcnt_blocks<Cfg::kDmaInsts, NS - 2>(nblk - 1 - blk);
     __syncthreads();
-    if (blk + 1 < nblk) {
-      issue_block(blk + 1, lane < RPW ? page_slot(page_next, off_next) : 0);
-      if (blk + 2 < nblk && lane < RPW) page_next = fetch_page(blk + 2, off_next);
+    if (blk + NS - 1 < nblk) {
+      page_slots(blk + NS - 1, page_n, slot);
+      issue_block(blk + NS - 1, slot);
+      if (blk + NS < nblk) fetch_pages(blk + NS, page_n);
     }
-    LDS_PTR(uint8_t) stage = lds + (uint32_t)(blk & 1) * L::kBlockBytes;
-    const int kv0 = c_start + blk * kBlockRows;
+    LDS_PTR(uint8_t) stage = lds + (uint32_t)(blk % NS) * L::kBlockBytes;
+    const int kv0 = c_start + blk * BN;
 
-    // ---- S^T[kv, head] = K Q^T for the 64 rows of the block (4 tiles of 16 kv rows).
-    // The reads walk (step, tile) with a ring of KD reads in flight; every
-    // read is followed by a scheduling barrier so that the compiler cannot
-    // hoist the whole block's reads (which would exhaust the registers).
-    f32x4_t sacc[4][HT];
+    // ---- S^T[kv, head] = K Q^T for the BN rows of the block (NT tiles of 16 kv rows).
+    // The reads walk (step, tile) with a ring of KD reads in flight.
+    f32x4_t sacc[NT];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) sacc[nt][ht] = f32x4_t{0, 0, 0, 0};
+    for (int nt = 0; nt < NT; ++nt) sacc[nt] = f32x4_t{0, 0, 0, 0};
     {
       constexpr int kSteps = FP8 ? 9 : 18;
       constexpr int kMainSteps = FP8 ? 8 : 16;  // steps whose slots lie in the main region
-      constexpr int kReads = kSteps * 4;
-      constexpr int KD = WPE == 2 ? 2 : (HT == 2 ? 3 : 8);
+      constexpr int kReads = kSteps * NT;
       u32x4_t kb[KD];
       auto kread = [&](int i) -> u32x4_t {
-        const int step = i >> 2, nt = i & 3, o = nt & 1;
+        const int step = i / NT, nt = i % NT, o = nt & 1;
         uint32_t off;
         if (step < kMainSteps) {
           off = k_main_base[o] + (uint32_t)(nt * 16 * L::kMainStride + step * 64);
@@ -421,77 +448,64 @@ void mla_decode_kernel(DecodeArgs a) {
       for (int i = 0; i < kReads; ++i) {
         if (i + KD - 1 < kReads) kb[(i + KD - 1) % KD] = kread(i + KD - 1);
         const u32x4_t raw = kb[i % KD];
-        const int step = i >> 2, nt = i & 3;
+        const int step = i / NT, nt = i % NT;
         if constexpr (FP8) {
           // 16 fp8 = d in [64 step + 16 g4, +16): two k-steps of 8
-          const bf16x8_t k0 = fp8x8_to_bf16x8(raw[0], raw[1]);
-          const bf16x8_t k1 = fp8x8_to_bf16x8(raw[2], raw[3]);
-#pragma unroll
-          for (int ht = 0; ht < HT; ++ht) {
-            sacc[nt][ht] = mfma16(k0, qf[ht][2 * step], sacc[nt][ht]);
-            sacc[nt][ht] = mfma16(k1, qf[ht][2 * step + 1], sacc[nt][ht]);
-          }
+          sacc[nt] = mfma16(fp8x8_to_bf16x8(raw[0], raw[1]), qf[2 * step], sacc[nt]);
+          sacc[nt] = mfma16(fp8x8_to_bf16x8(raw[2], raw[3]), qf[2 * step + 1], sacc[nt]);
         } else {
-#pragma unroll
-          for (int ht = 0; ht < HT; ++ht) sacc[nt][ht] = mfma16(__builtin_bit_cast(bf16x8_t, raw), qf[ht][step], sacc[nt][ht]);
+          sacc[nt] = mfma16(__builtin_bit_cast(bf16x8_t, raw), qf[step], sacc[nt]);
         }
         MLA_STEP_BARRIER();
       }
     }
 
-    // ---- mask, online softmax (lane = one head row per tile, 16 kv values per lane)
-    bf16x8_t pf[HT][2];
-    float alpha[HT];
-    bool any_up = false;
-    // score row 4g4+r of tile nt is cache row kv0 + nt*16 + 2r + (pg ^ (nt&1)),
-    // pg = 8(g4&1) + (g4>>1); compare the compile-time part against a limit.
-    const int pg = 8 * (g4 & 1) + (g4 >> 1);
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      const int lim0 = vis_end[ht] - kv0 - pg, lim1 = vis_end[ht] - kv0 - (pg ^ 1);
+    // ---- mask, online softmax (lane = one head row, 4*NT kv values per lane)
+    bf16x8_t pf[NU];
+    float alpha;
+    bool up;
+    {
+      const int lim0 = vis_end - kv0 - pg, lim1 = vis_end - kv0 - (pg ^ 1);
       float mx = -__builtin_inff();
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float v = sacc[nt][ht][r] * sscale;
+          float v = sacc[nt][r] * sscale;
           v = nt * 16 + 2 * r < ((nt & 1) ? lim1 : lim0) ? v : -__builtin_inff();
-          sacc[nt][ht][r] = v;
+          sacc[nt][r] = v;
           mx = fmaxf(mx, v);
         }
       mx = wave_max_16x4(mx);
-      const float old = m_ref[ht];
-      const bool up = mx > old + kRescaleSlack;
+      const float old = m_ref;
+      up = mx > old + kRescaleSlack;
       const float m_new = up ? mx : old;
-      alpha[ht] = up ? __builtin_amdgcn_exp2f(old - m_new) : 1.0f;  // old = -inf gives 0
-      any_up |= up;
-      m_ref[ht] = m_new;
+      alpha = up ? __builtin_amdgcn_exp2f(old - m_new) : 1.0f;  // old = -inf gives 0
+      m_ref = m_new;
       const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;
       float psum = 0.0f;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(sacc[nt][ht][r] - m_use);
-          sacc[nt][ht][r] = p;
+          const float p = __builtin_amdgcn_exp2f(sacc[nt][r] - m_use);
+          sacc[nt][r] = p;
           psum += p;
         }
-      l_part[ht] = l_part[ht] * alpha[ht] + psum;
+      l_part = l_part * alpha + psum;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < NU; ++u) {
         u32x4_t w;
-        w[0] = pack_bf16x2(sacc[2 * u][ht][0], sacc[2 * u][ht][1]);
-        w[1] = pack_bf16x2(sacc[2 * u][ht][2], sacc[2 * u][ht][3]);
-        w[2] = pack_bf16x2(sacc[2 * u + 1][ht][0], sacc[2 * u + 1][ht][1]);
-        w[3] = pack_bf16x2(sacc[2 * u + 1][ht][2], sacc[2 * u + 1][ht][3]);
-        pf[ht][u] = __builtin_bit_cast(bf16x8_t, w);
+        w[0] = pack_bf16x2(sacc[2 * u][0], sacc[2 * u][1]);
+        w[1] = pack_bf16x2(sacc[2 * u][2], sacc[2 * u][3]);
+        w[2] = pack_bf16x2(sacc[2 * u + 1][0], sacc[2 * u + 1][1]);
+        w[3] = pack_bf16x2(sacc[2 * u + 1][2], sacc[2 * u + 1][3]);
+        pf[u] = __builtin_bit_cast(bf16x8_t, w);
       }
     }
-    if (__builtin_amdgcn_ballot_w64(any_up)) {
+    if (__builtin_amdgcn_ballot_w64(up)) {
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-        for (int nt = 0; nt < 32; ++nt) o_acc[nt][ht] *= alpha[ht];
+      for (int nt = 0; nt < 32; ++nt) o_acc[nt] *= alpha;
     }
 
     // ---- O^T[n, head] += V^T P^T ; V^T fragments by transposed LDS reads.
@@ -499,7 +513,7 @@ void mla_decode_kernel(DecodeArgs a) {
     // then 32u + 16 + pi_1(4g4 + r); the V^T fragment holds the same rows, in
     // the same order, for its latent column.
     {
-      constexpr int VD = WPE == 2 ? 2 : (HT == 2 ? 3 : 8);  // V^T fragments in flight
+      constexpr int kReads = 32 * NU;
       u32x4_t vb[VD];
       auto vread = [&](int j) -> u32x4_t {
         const int u = j >> 5, nt = j & 31;
@@ -527,43 +541,41 @@ void mla_decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < VD - 1; ++j) vb[j] = vread(j);
 #pragma unroll
-      for (int j = 0; j < 64; ++j) {
-        if (j + VD - 1 < 64) vb[(j + VD - 1) % VD] = vread(j + VD - 1);
+      for (int j = 0; j < kReads; ++j) {
+        if (j + VD - 1 < kReads) vb[(j + VD - 1) % VD] = vread(j + VD - 1);
         const u32x4_t w = vb[j % VD];
         const bf16x8_t vf = FP8 ? fp8x8_to_bf16x8(w[0], w[1]) : __builtin_bit_cast(bf16x8_t, w);
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) o_acc[j & 31][ht] = mfma16(vf, pf[ht][j >> 5], o_acc[j & 31][ht]);
+        o_acc[j & 31] = mfma16(vf, pf[j >> 5], o_acc[j & 31]);
         MLA_STEP_BARRIER();
       }
     }
   }
+  if (bad_page && lane == 0) atomicOr(a.status, MLA_DEV_PAGE_OUT_OF_RANGE);
 
   // ---- epilogue: normalise, then the final row (single chunk) or a partial record
+  const float l = wave_sum_16x4(l_part);
+  const bool empty = !(l > 0.0f);
+  const float inv = empty ? 0.0f : a.out_scale / l;
+  const float lse2 = empty ? -__builtin_inff() : m_ref + __log2f(l);
+  if (!row_ok) return;
+  if (n_b == 1) {
+    uint16_t* orow = a.out + (int64_t)row_out * kLatentDim;
 #pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    const float l = wave_sum_16x4(l_part[ht]);
-    const bool empty = !(l > 0.0f);
-    const float inv = empty ? 0.0f : a.out_scale / l;
-    const float lse2 = empty ? -__builtin_inff() : m_ref[ht] + __log2f(l);
-    if (!row_ok[ht]) continue;
-    if (n_b == 1) {
-      uint16_t* orow = a.out + (int64_t)row_out[ht] * kLatentDim;
-#pragma unroll
-      for (int nt = 0; nt < 32; ++nt) {
-        const f32x4_t o = o_acc[nt][ht] * inv;
-        u32x2_t w;
-        w[0] = pack_bf16x2(o[0], o[1]);
-        w[1] = pack_bf16x2(o[2], o[3]);
-        *(u32x2_t*)(orow + nt * 16 + 4 * g4) = w;
-      }
-      if (a.lse && g4 == 0) a.lse[row_out[ht]] = lse2 * kLn2;
-    } else {
-      const int64_t rec = (int64_t)a.partbase[b] + (int64_t)grp * n_b + chunk;
-      float* prow = a.part_out + (rec * a.rows_per_group + row_rr[ht]) * kLatentDim;
-#pragma unroll
-      for (int nt = 0; nt < 32; ++nt) *(f32x4_t*)(prow + nt * 16 + 4 * g4) = o_acc[nt][ht] * inv;
-      if (g4 == 0) a.part_lse[rec * a.rows_per_group + row_rr[ht]] = lse2;
+    for (int nt = 0; nt < 32; ++nt) {
+      const f32x4_t o = o_acc[nt] * inv;
+      u32x2_t w;
+      w[0] = pack_bf16x2(o[0], o[1]);
+      w[1] = pack_bf16x2(o[2], o[3]);
+      *(u32x2_t*)(orow + nt * 16 + 4 * g4) = w;
     }
+    if (a.lse && g4 == 0) a.lse[row_out] = lse2 * kLn2;
+  } else {
+    const int rr = wave * 16 + i16;
+    const int64_t rec = (int64_t)a.partbase[b] + (int64_t)grp * n_b + chunk;
+    float* prow = a.part_out + (rec * a.rows_per_group + rr) * kLatentDim;
+#pragma unroll
+    for (int nt = 0; nt < 32; ++nt) *(f32x4_t*)(prow + nt * 16 + 4 * g4) = o_acc[nt] * inv;
+    if (g4 == 0) a.part_lse[rec * a.rows_per_group + rr] = lse2;
   }
 }
 
@@ -663,9 +675,9 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
     a.lse[orow] = empty ? -__builtin_inff() : (M + __log2f(total)) * kLn2;
 }
 
-template <bool FP8, int NW, int HT, int WPE>
+template <bool FP8, int NW, int BN, int NS, int WPE, int KD, int VD>
 int launch_decode_t(const DecodeArgs& a, int gx, int gy, int gz, hipStream_t st) {
-  hipLaunchKernelGGL((mla_decode_kernel<FP8, NW, HT, WPE>), dim3(gx, gy, gz), dim3(NW * 64), 0, st, a);
+  hipLaunchKernelGGL((mla_decode_kernel<FP8, NW, BN, NS, WPE, KD, VD>), dim3(gx, gy, gz), dim3(NW * 64), 0, st, a);
   return (int)hipGetLastError();
 }
 
@@ -676,17 +688,20 @@ int launch_plan(const PlanArgs& a, void* stream) {
   return (int)hipGetLastError();
 }
 
-// Tile classes: 16, 32, 64, 128 rows -> 1, 2, 4, 8 waves of one 16-row head
-// tile. The 128-row tile runs two waves per SIMD (256 registers each); the
-// smaller tiles one wave per SIMD per workgroup.
+// Tile classes: 16, 32 and 64 rows run the 64-row kernel (4 waves of one
+// 16-row head tile, one wave per SIMD, rows past the tile masked); 128 rows run
+// 8 waves (two per SIMD, 256 registers each). All on 32-row blocks, with as
+// many stages as the LDS holds.
 int launch_decode(const DecodeArgs& a, int kv_dtype, int tile_class, int gx, int gy, int gz, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const bool fp8 = kv_dtype == MLA_KV_FP8_E4M3FN;
   switch (tile_class) {
-    case 0: return fp8 ? launch_decode_t<true, 1, 1, 1>(a, gx, gy, gz, st) : launch_decode_t<false, 1, 1, 1>(a, gx, gy, gz, st);
-    case 1: return fp8 ? launch_decode_t<true, 2, 1, 1>(a, gx, gy, gz, st) : launch_decode_t<false, 2, 1, 1>(a, gx, gy, gz, st);
-    case 2: return fp8 ? launch_decode_t<true, 4, 1, 1>(a, gx, gy, gz, st) : launch_decode_t<false, 4, 1, 1>(a, gx, gy, gz, st);
-    case 3: return fp8 ? launch_decode_t<true, 8, 1, 2>(a, gx, gy, gz, st) : launch_decode_t<false, 8, 1, 2>(a, gx, gy, gz, st);
+    case 0:
+    case 1:
+    case 2: return fp8 ? launch_decode_t<true, 4, 32, 8, 1, 8, 8>(a, gx, gy, gz, st)
+                       : launch_decode_t<false, 4, 32, 4, 1, 8, 8>(a, gx, gy, gz, st);
+    case 3: return fp8 ? launch_decode_t<true, 8, 32, 8, 2, 3, 3>(a, gx, gy, gz, st)
+                       : launch_decode_t<false, 8, 32, 4, 2, 3, 3>(a, gx, gy, gz, st);
   }
   return (int)hipErrorInvalidValue;
 }

@@ -112,7 +112,7 @@ def test_tiny_workload_forced_split_exercises_the_combine():
 GRID = []
 for kv_dtype in ("bf16", "fp8_e4m3fn"):
     for (S, H, causal) in ((1, 12, False), (1, 16, False), (4, 16, True), (2, 32, False), (1, 128, False),
-                           (4, 32, True), (3, 5, True), (1, 40, False)):
+                           (4, 32, True), (3, 5, True), (1, 40, False), (2, 16, True), (1, 20, False)):
         for P in (1, 16, 64):
             GRID.append((kv_dtype, S, H, causal, P))
 
