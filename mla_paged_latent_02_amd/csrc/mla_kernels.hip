@@ -140,10 +140,13 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(PlanArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode. One workgroup = one (chunk, head group, sequence); NW waves, each
-// owning one 16-row head tile (its query fragments and its 16 x 512 fp32
-// output stay in registers for the whole chunk); all waves share each block
-// of BN cache rows in LDS. NS blocks are in flight in an LDS ring.
+// Decode. One workgroup = one (chunk, head group, sequence) with HW x KW
+// waves. Wave (hw, kw) owns head tile hw (16 tile rows: its query fragments
+// and its 16 x 512 fp32 output stay in registers for the whole chunk) and
+// cache rows [32 kw, 32 kw + 32) of every block of BN = 32 KW rows, with its
+// own online-softmax state. The KW states of a head tile are merged through
+// LDS at the end of the chunk. All waves load each block into an LDS ring of
+// NS stages; a block's rows are gathered by every wave together.
 //
 // LDS block layout (one stage, BN cache rows):
 //   main region: row r at r*kMainStride holds the 512 latent elements (the V
@@ -170,18 +173,23 @@ struct RowLayout {
   static __device__ __forceinline__ int tail_xor(int r) { return FP8 ? ((r >> 2) & 3) : ((r >> 1) & 7); }
 };
 
-template <bool FP8, int NW, int BN, int NS>
+template <bool FP8, int HW, int KW, int NS>
 struct DecodeCfg {
-  using L = RowLayout<FP8, BN>;
-  static constexpr int kLdsBytes = NS * L::kBlockBytes;
-  static constexpr int kRowsPerWave = BN / NW;  // rows each wave gathers per block
+  static constexpr int kWaves = HW * KW;
+  static constexpr int kBlockN = 32 * KW;  // cache rows per block
+  using L = RowLayout<FP8, kBlockN>;
+  static constexpr int kRingBytes = NS * L::kBlockBytes;
+  // merge area after the loop: every wave's 16 x 512 fp32 output, then its max and sum per head
+  static constexpr int kMergeBytes = KW > 1 ? kWaves * (32 * 64 * 16 + 2 * 16 * 4) : 0;
+  static constexpr int kLdsBytes = kRingBytes > kMergeBytes ? kRingBytes : kMergeBytes;
+  static constexpr int kRowsPerWave = kBlockN / kWaves;  // rows each wave gathers per block
   static constexpr int kTailRowsPerInst = 64 / L::kTailSlots;
   static constexpr int kTailInsts = (kRowsPerWave + kTailRowsPerInst - 1) / kTailRowsPerInst;
   static constexpr int kDmaInsts = kRowsPerWave + kTailInsts;  // vector-memory instructions per wave per block
-  static constexpr int kTiles = BN / 16;                       // score tiles per block
-  static constexpr int kKSteps = BN / 32;                      // PV k-steps per block
+  static constexpr int kTiles = 2;                             // score tiles of 16 rows per wave per block
+  static constexpr int kKSteps = 1;                            // PV k-steps of 32 rows per wave per block
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-  static_assert(kRowsPerWave >= 1 && BN % 32 == 0, "row split");
+  static_assert(kRowsPerWave >= 1 && kBlockN % kWaves == 0, "row split");
   static_assert((NS - 2) * kDmaInsts <= 63, "vmcnt range");
 };
 
@@ -224,11 +232,13 @@ __device__ __forceinline__ int perm_row(int m, int odd) {
   return (2 * r + 8 * (g & 1) + (g >> 1)) ^ odd;
 }
 
-template <bool FP8, int NW, int BN, int NS, int WPE, int KD, int VD>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+template <bool FP8, int HW, int KW, int NS, int WPE, int KD, int VD>
+__global__ __launch_bounds__(HW * KW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void mla_decode_kernel(DecodeArgs a) {
-  using Cfg = DecodeCfg<FP8, NW, BN, NS>;
+  using Cfg = DecodeCfg<FP8, HW, KW, NS>;
   using L = typename Cfg::L;
+  constexpr int NW = Cfg::kWaves;
+  constexpr int BN = Cfg::kBlockN;
   constexpr int RPW = Cfg::kRowsPerWave;
   constexpr int NT = Cfg::kTiles;
   constexpr int NU = Cfg::kKSteps;
@@ -242,6 +252,8 @@ void mla_decode_kernel(DecodeArgs a) {
   const int n_b = a.nchunks[b];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keep it scalar
+  const int hw = wave % HW;   // head tile
+  const int kw = wave / HW;   // row slice of each block
   const int i16 = lane & 15;  // MFMA column: head row within the wave's 16-row tile
   const int g4 = lane >> 4;   // MFMA k-group
 
@@ -272,7 +284,7 @@ void mla_decode_kernel(DecodeArgs a) {
   int vis_end, row_out;
   bool row_ok;
   {
-    const int rr = wave * 16 + i16;
+    const int rr = hw * 16 + i16;
     const int tok = rr / a.heads_per_group;
     const int head = grp * a.heads_per_group + rr % a.heads_per_group;
     row_ok = rr < a.rows_per_group && head < a.num_heads;
@@ -302,18 +314,20 @@ void mla_decode_kernel(DecodeArgs a) {
   for (int nt = 0; nt < 32; ++nt) o_acc[nt] = f32x4_t{0, 0, 0, 0};
 
   // ---- page-gathered block loads.
-  // Page ids are read with scalar loads (wave-uniform addresses), so the only
-  // vector-memory instructions in the loop are the Cfg::kDmaInsts DMA
-  // instructions per block and the ring can wait for its oldest block alone.
   // Row r of the wave's share of block blk is cache row
   // min(c_start + blk*BN + wave*RPW + r, c_end - 1): rows past the chunk repeat
-  // its last row, whose scores are masked.
-  const __attribute__((address_space(4))) int32_t* page_ids =
-      (const __attribute__((address_space(4))) int32_t*)a.kv_page_indices;
+  // its last row, whose scores are masked. The page ids come either
+  //  - (ring of more than two stages) from scalar loads, so that the only
+  //    vector-memory instructions in the loop are the Cfg::kDmaInsts DMA
+  //    instructions per block and the ring can wait for its oldest block alone;
+  //  - (two stages) from one vector load per block (lane r: row r), issued
+  //    right after the previous block's DMA: the loop waits for all its loads
+  //    at the top anyway, and no scalar register has to hold a block of ids.
+  constexpr bool kVecPages = NS == 2;
   const uint32_t magic = a.page_div_magic;
+  const uint8_t* cache = a.cache;
   bool bad_page = false;
-  auto row_page_pos = [&](int blk, int r, int& q, int& rem) {
-    const int kv = __builtin_amdgcn_readfirstlane(min(c_start + blk * BN + wave * RPW + r, c_end - 1));
+  auto page_pos = [&](int kv, int& q, int& rem) {
     q = (int)__umulhi((uint32_t)kv, magic);
     rem = kv - q * P;
     if (rem >= P) {
@@ -321,55 +335,87 @@ void mla_decode_kernel(DecodeArgs a) {
       rem -= P;
     }
   };
+  auto row_kv = [&](int blk, int r) { return min(c_start + blk * BN + wave * RPW + r, c_end - 1); };
+  const int tslot = lane % L::kTailSlots;
+  const int trow = lane / L::kTailSlots;
+  // main part of row r: one instruction; lane l fetches the row's 16-byte slot l
+  // (bf16: 64 slots; fp8: 32 slots, upper half of the wave idle)
+  auto issue_main_row = [&](int blk, int r, int slot_s) {
+    const uint32_t stage_off = (uint32_t)(blk % NS) * L::kBlockBytes;
+    const uint8_t* src = cache + (int64_t)slot_s * L::kRowBytes + (lane << 4);
+    const uint32_t dst =
+        __builtin_amdgcn_readfirstlane(lds_base + stage_off + (uint32_t)((wave * RPW + r) * L::kMainStride));
+    if (FP8 ? lane < 32 : true) dma16(src, dst);
+  };
+  // rope tails: instruction m covers kTailRowsPerInst rows x kTailSlots slots;
+  // sv is the slot of this lane's row
+  auto issue_tail = [&](int blk, int m, int sv) {
+    const uint32_t stage_off = (uint32_t)(blk % NS) * L::kBlockBytes;
+    const int r = wave * RPW + m * Cfg::kTailRowsPerInst + trow;
+    const int logical = tslot ^ L::tail_xor(r);
+    const uint8_t* src = cache + (int64_t)sv * L::kRowBytes + L::kMainBytes + (logical << 4);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(
+        lds_base + stage_off + (uint32_t)(L::kTailBase + (wave * RPW + m * Cfg::kTailRowsPerInst) * L::kTailBytes));
+    if (m * Cfg::kTailRowsPerInst + trow < RPW) dma16(src, dst);
+  };
+
+  // scalar page ids
+  const __attribute__((address_space(4))) int32_t* page_ids =
+      (const __attribute__((address_space(4))) int32_t*)a.kv_page_indices;
   auto fetch_pages = [&](int blk, int (&page)[RPW]) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       int q, rem;
-      row_page_pos(blk, r, q, rem);
+      page_pos(__builtin_amdgcn_readfirstlane(row_kv(blk, r)), q, rem);
       page[r] = page_ids[page_base + q];
     }
   };
-  auto page_slots = [&](int blk, const int (&page)[RPW], int (&slot)[RPW]) {
+  auto issue_block = [&](int blk, const int (&page)[RPW]) {
+    int slot[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       int q, rem;
-      row_page_pos(blk, r, q, rem);
+      page_pos(__builtin_amdgcn_readfirstlane(row_kv(blk, r)), q, rem);
       int pg = page[r];
       if ((uint32_t)pg >= (uint64_t)a.num_pages) {
         bad_page = true;
         pg = 0;
       }
       slot[r] = pg * P + rem;
+      issue_main_row(blk, r, slot[r]);
     }
-  };
-  const uint8_t* cache = a.cache;
-  auto issue_block = [&](int blk, const int (&slot)[RPW]) {
-    const uint32_t stage_off = (uint32_t)(blk % NS) * L::kBlockBytes;
-    const int r_base = wave * RPW;
-    // main: one instruction per row; lane l fetches the row's 16-byte slot l
-    // (bf16: 64 slots; fp8: 32 slots, upper half of the wave idle)
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const uint8_t* src = cache + (int64_t)slot[r] * L::kRowBytes + (lane << 4);
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_base + stage_off + (uint32_t)((r_base + r) * L::kMainStride));
-      if (FP8 ? lane < 32 : true) dma16(src, dst);
-    }
-    // tail: kTailRowsPerInst rows x kTailSlots slots per instruction
-    const int tslot = lane % L::kTailSlots;
-    const int trow = lane / L::kTailSlots;
 #pragma unroll
     for (int m = 0; m < Cfg::kTailInsts; ++m) {
       int sv = slot[m * Cfg::kTailRowsPerInst];
 #pragma unroll
       for (int k = 1; k < Cfg::kTailRowsPerInst; ++k)
         if (m * Cfg::kTailRowsPerInst + k < RPW && trow == k) sv = slot[m * Cfg::kTailRowsPerInst + k];
-      const int r = r_base + m * Cfg::kTailRowsPerInst + trow;
-      const int logical = tslot ^ L::tail_xor(r);
-      const uint8_t* src = cache + (int64_t)sv * L::kRowBytes + L::kMainBytes + (logical << 4);
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(
-          lds_base + stage_off + (uint32_t)(L::kTailBase + (r_base + m * Cfg::kTailRowsPerInst) * L::kTailBytes));
-      if (m * Cfg::kTailRowsPerInst + trow < RPW) dma16(src, dst);
+      issue_tail(blk, m, sv);
     }
+  };
+
+  // vector page ids: lane r < RPW holds the page id of row r of the next block
+  int v_page = 0;
+  const int my_row = lane < RPW ? lane : RPW - 1;
+  auto fetch_pages_v = [&](int blk) {
+    int q, rem;
+    page_pos(row_kv(blk, my_row), q, rem);
+    v_page = a.kv_page_indices[page_base + q];
+  };
+  auto issue_block_v = [&](int blk) {
+    int q, rem;
+    page_pos(row_kv(blk, my_row), q, rem);
+    int pg = v_page;
+    if ((uint32_t)pg >= (uint64_t)a.num_pages) {
+      bad_page = true;
+      pg = 0;
+    }
+    const int slot_v = pg * P + rem;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) issue_main_row(blk, r, __builtin_amdgcn_readlane(slot_v, r));
+#pragma unroll
+    for (int m = 0; m < Cfg::kTailInsts; ++m)
+      issue_tail(blk, m, __builtin_amdgcn_ds_bpermute((m * Cfg::kTailRowsPerInst + trow) << 2, slot_v));
   };
 
   // Per-lane LDS offsets that do not change over the loop; each access adds a
@@ -394,16 +440,21 @@ void mla_decode_kernel(DecodeArgs a) {
   }
 
   // ---- prologue: blocks 0 .. NS-2 in flight, pages of block NS-1 fetched
-  int page_n[RPW], slot[RPW];
+  int page_n[kVecPages ? 1 : RPW];
+  if constexpr (kVecPages) {
+    fetch_pages_v(0);
+    issue_block_v(0);
+    if (1 < nblk) fetch_pages_v(1);
+  } else {
 #pragma unroll
-  for (int i = 0; i < NS - 1; ++i) {
-    if (i < nblk) {
-      fetch_pages(i, page_n);
-      page_slots(i, page_n, slot);
-      issue_block(i, slot);
+    for (int i = 0; i < NS - 1; ++i) {
+      if (i < nblk) {
+        fetch_pages(i, page_n);
+        issue_block(i, page_n);
+      }
     }
+    if (NS - 1 < nblk) fetch_pages(NS - 1, page_n);
   }
-  if (NS - 1 < nblk) fetch_pages(NS - 1, page_n);
 
   const float sscale = a.score_scale_log2;
   const int pg = 8 * (g4 & 1) + (g4 >> 1);  // score row 4g4+r of a tile is cache row 2r + (pg ^ (nt&1))
@@ -413,14 +464,21 @@ void mla_decode_kernel(DecodeArgs a) {
     wait_vmcnt_blocks<Cfg::kDmaInsts, NS - 2>(nblk - 1 - blk);
     __syncthreads();
     if (blk + NS - 1 < nblk) {
-      page_slots(blk + NS - 1, page_n, slot);
-      issue_block(blk + NS - 1, slot);
-      if (blk + NS < nblk) fetch_pages(blk + NS, page_n);
+      if constexpr (kVecPages) {
+        issue_block_v(blk + 1);
+        if (blk + 2 < nblk) fetch_pages_v(blk + 2);
+      } else {
+        issue_block(blk + NS - 1, page_n);
+        if (blk + NS < nblk) fetch_pages(blk + NS, page_n);
+      }
     }
     LDS_PTR(uint8_t) stage = lds + (uint32_t)(blk % NS) * L::kBlockBytes;
-    const int kv0 = c_start + blk * BN;
+    // this wave's 32 rows of the block: main rows at mstage, rope tails at tstage
+    LDS_PTR(uint8_t) mstage = stage + (uint32_t)(kw * 32 * L::kMainStride);
+    LDS_PTR(uint8_t) tstage = stage + (uint32_t)(L::kTailBase + kw * 32 * L::kTailBytes);
+    const int kv0 = c_start + blk * BN + kw * 32;
 
-    // ---- S^T[kv, head] = K Q^T for the BN rows of the block (NT tiles of 16 kv rows).
+    // ---- S^T[kv, head] = K Q^T for the wave's 32 rows of the block (NT tiles of 16 kv rows).
     // The reads walk (step, tile) with a ring of KD reads in flight.
     f32x4_t sacc[NT];
 #pragma unroll
@@ -432,15 +490,11 @@ void mla_decode_kernel(DecodeArgs a) {
       u32x4_t kb[KD];
       auto kread = [&](int i) -> u32x4_t {
         const int step = i / NT, nt = i % NT, o = nt & 1;
-        uint32_t off;
-        if (step < kMainSteps) {
-          off = k_main_base[o] + (uint32_t)(nt * 16 * L::kMainStride + step * 64);
-        } else {
-          const int s2 = 4 * (step - kMainSteps) + g4;  // logical tail slot of this lane
-          const int pr = perm_row(i16, o);
-          off = L::kTailBase + (uint32_t)((nt * 16 + pr) * L::kTailBytes) + ((uint32_t)(s2 ^ L::tail_xor(pr)) << 4);
-        }
-        return lds_b128(stage, off);
+        if (step < kMainSteps)
+          return lds_b128(mstage, k_main_base[o] + (uint32_t)(nt * 16 * L::kMainStride + step * 64));
+        const int s2 = 4 * (step - kMainSteps) + g4;  // logical tail slot of this lane
+        const int pr = perm_row(i16, o);
+        return lds_b128(tstage, (uint32_t)((nt * 16 + pr) * L::kTailBytes) + ((uint32_t)(s2 ^ L::tail_xor(pr)) << 4));
       };
 #pragma unroll
       for (int i = 0; i < KD - 1; ++i) kb[i] = kread(i);
@@ -520,15 +574,15 @@ void mla_decode_kernel(DecodeArgs a) {
         u32x4_t w;
         if constexpr (FP8) {
           const uint32_t off = v_base_lo + (uint32_t)(32 * u * L::kMainStride + nt * 16);
-          const i32x2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(i32x2_t))(stage + off));
+          const i32x2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(i32x2_t))(mstage + off));
           w[0] = (unsigned)raw[0];
           w[1] = (unsigned)raw[1];
           w[2] = 0;
           w[3] = 0;
         } else {
           const uint32_t imm = (uint32_t)(32 * u * L::kMainStride + nt * 32);
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4_t))(stage + v_base_lo + imm));
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4_t))(stage + v_base_hi + imm));
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4_t))(mstage + v_base_lo + imm));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4_t))(mstage + v_base_hi + imm));
           const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
           const u32x2_t h2 = __builtin_bit_cast(u32x2_t, hi);
           w[0] = l2[0];
@@ -550,51 +604,94 @@ void mla_decode_kernel(DecodeArgs a) {
       }
     }
   }
-  if (bad_page && lane == 0) atomicOr(a.status, MLA_DEV_PAGE_OUT_OF_RANGE);
+  if (__builtin_amdgcn_ballot_w64(bad_page) && lane == 0) atomicOr(a.status, MLA_DEV_PAGE_OUT_OF_RANGE);
 
-  // ---- epilogue: normalise, then the final row (single chunk) or a partial record
-  const float l = wave_sum_16x4(l_part);
-  const bool empty = !(l > 0.0f);
-  const float inv = empty ? 0.0f : a.out_scale / l;
-  const float lse2 = empty ? -__builtin_inff() : m_ref + __log2f(l);
+  // ---- epilogue. Each head tile has KW partial states (m_ref, l, o_acc) over
+  // disjoint row sets, all relative to their own reference max. With KW > 1
+  // they go through LDS and wave (hw, kw) merges latent columns
+  // [512 kw / KW, 512 (kw + 1) / KW) of head tile hw.
+  constexpr int kTilesOut = 32 / KW;  // 16-column output tiles per wave
+  float l_tot = wave_sum_16x4(l_part);
+  float m_fin = m_ref;
+  f32x4_t o_out[kTilesOut];
+  if constexpr (KW == 1) {
+#pragma unroll
+    for (int nt = 0; nt < 32; ++nt) o_out[nt] = o_acc[nt];
+  } else {
+    __syncthreads();  // every wave is done with the ring
+    LDS_PTR(f32x4_t) ox = (LDS_PTR(f32x4_t))lds;                        // [NW][32][64]
+    LDS_PTR(float) mlx = (LDS_PTR(float))(lds + NW * 32 * 64 * 16);   // [NW][2][16]
+#pragma unroll
+    for (int nt = 0; nt < 32; ++nt) ox[(wave * 32 + nt) * 64 + lane] = o_acc[nt];
+    if (g4 == 0) {
+      mlx[wave * 32 + i16] = m_ref;
+      mlx[wave * 32 + 16 + i16] = l_tot;
+    }
+    __syncthreads();
+    float ms[KW], wt[KW];
+    m_fin = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < KW; ++k) {
+      ms[k] = mlx[(hw + HW * k) * 32 + i16];
+      m_fin = fmaxf(m_fin, ms[k]);
+    }
+    l_tot = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KW; ++k) {
+      wt[k] = ms[k] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(ms[k] - m_fin);
+      l_tot += wt[k] * mlx[(hw + HW * k) * 32 + 16 + i16];
+    }
+#pragma unroll
+    for (int j = 0; j < kTilesOut; ++j) {
+      const int nt = kw * kTilesOut + j;
+      f32x4_t acc = f32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int k = 0; k < KW; ++k) acc += wt[k] * ox[((hw + HW * k) * 32 + nt) * 64 + lane];
+      o_out[j] = acc;
+    }
+  }
+  const bool empty = !(l_tot > 0.0f);
+  const float inv = empty ? 0.0f : a.out_scale / l_tot;
+  const float lse2 = empty ? -__builtin_inff() : m_fin + __log2f(l_tot);
   if (!row_ok) return;
+  const int nt0 = kw * kTilesOut;
   if (n_b == 1) {
     uint16_t* orow = a.out + (int64_t)row_out * kLatentDim;
 #pragma unroll
-    for (int nt = 0; nt < 32; ++nt) {
-      const f32x4_t o = o_acc[nt] * inv;
+    for (int j = 0; j < kTilesOut; ++j) {
+      const f32x4_t o = o_out[j] * inv;
       u32x2_t w;
       w[0] = pack_bf16x2(o[0], o[1]);
       w[1] = pack_bf16x2(o[2], o[3]);
-      *(u32x2_t*)(orow + nt * 16 + 4 * g4) = w;
+      *(u32x2_t*)(orow + (nt0 + j) * 16 + 4 * g4) = w;
     }
-    if (a.lse && g4 == 0) a.lse[row_out] = lse2 * kLn2;
+    if (a.lse && kw == 0 && g4 == 0) a.lse[row_out] = lse2 * kLn2;
   } else {
-    const int rr = wave * 16 + i16;
+    const int rr = hw * 16 + i16;
     const int64_t rec = (int64_t)a.partbase[b] + (int64_t)grp * n_b + chunk;
     float* prow = a.part_out + (rec * a.rows_per_group + rr) * kLatentDim;
 #pragma unroll
-    for (int nt = 0; nt < 32; ++nt) *(f32x4_t*)(prow + nt * 16 + 4 * g4) = o_acc[nt] * inv;
-    if (g4 == 0) a.part_lse[rec * a.rows_per_group + rr] = lse2;
+    for (int j = 0; j < kTilesOut; ++j) *(f32x4_t*)(prow + (nt0 + j) * 16 + 4 * g4) = o_out[j] * inv;
+    if (kw == 0 && g4 == 0) a.part_lse[rec * a.rows_per_group + rr] = lse2;
   }
 }
 
 // ---------------------------------------------------------------------------
 // Combine: one workgroup (256 threads) per (column block of CB columns, tile
-// row, sequence x group). Phase 1 turns every partial lse into a weight
-// 2^(lse_c - M) in LDS; phase 2 has 1024/CB streams of threads, each thread
-// owning 4 columns, accumulate the weighted partial outputs of chunks
-// stream, stream + nstreams, ... with independent loads; phase 3 sums the
-// streams. CB shrinks when there are few rows to merge, so that many
-// workgroups share a long list of chunks.
-constexpr int kCombineMaxChunks = 2048;  // chunks weighed per pass of phase 1
-
+// row, sequence x group), in a single pass over the partial records: the
+// threads form 1024/CB streams of CB/4 threads (4 columns each); a stream
+// walks chunks stream, stream + nstreams, ... keeping a running maximum m,
+// weight sum s and weighted column sums, so that the lse and the partial
+// output of a chunk are loaded together. The streams are then merged through
+// LDS. CB shrinks when there are few rows to merge, so that many workgroups
+// share a long list of chunks.
 template <int CB>
 __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
   constexpr int kThreadsPerChunk = CB / 4;
   constexpr int kStreams = 256 / kThreadsPerChunk;
-  __shared__ float w_lds[kCombineMaxChunks];
-  __shared__ float red[256];
+  constexpr int kUnroll = 4;
+  __shared__ float m_lds[kStreams], s_lds[kStreams], w_lds[kStreams];
+  __shared__ float total_lds;
   __shared__ __attribute__((aligned(16))) float acc_lds[kStreams][CB];
   const int colblk = blockIdx.x;
   const int rr = blockIdx.y;
@@ -606,78 +703,77 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
   const int head = grp * a.heads_per_group + rr % a.heads_per_group;
   if (head >= a.num_heads) return;
   const int tid = threadIdx.x;
-  const int64_t rec0 = (int64_t)a.partbase[b] + (int64_t)grp * n_b;
-  const int nw = min(n_b, kCombineMaxChunks);
-
-  // ---- phase 1: weights. A chunk with no visible row has lse = -inf (weight 0).
-  float m = -__builtin_inff();
-  for (int c = tid; c < n_b; c += 256) m = fmaxf(m, a.part_lse[(rec0 + c) * a.rows_per_group + rr]);
-  red[tid] = m;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  const bool empty = M == -__builtin_inff();
-  __syncthreads();
-  float wsum = 0.0f;
-  for (int c = tid; c < n_b; c += 256) {
-    const float w = empty ? 0.0f : __builtin_amdgcn_exp2f(a.part_lse[(rec0 + c) * a.rows_per_group + rr] - M);
-    wsum += w;
-    if (c < nw) w_lds[c] = w;
-  }
-  red[tid] = wsum;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) red[tid] += red[tid + off];
-    __syncthreads();
-  }
-  const float total = red[0];
-
-  // ---- phase 2: weighted sum of the partial outputs
   const int stream = tid / kThreadsPerChunk;
-  const int col = colblk * CB + (tid % kThreadsPerChunk) * 4;
-  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  const float* base = a.part_out + (rec0 * a.rows_per_group + rr) * kLatentDim + col;
+  const int quad = tid % kThreadsPerChunk;
+  const int64_t rec0 = (int64_t)a.partbase[b] + (int64_t)grp * n_b;
+  const float* lse_base = a.part_lse + rec0 * a.rows_per_group + rr;
+  const float* out_base = a.part_out + (rec0 * a.rows_per_group + rr) * kLatentDim + colblk * CB + quad * 4;
   const int64_t rec_stride = (int64_t)a.rows_per_group * kLatentDim;
-  for (int c0 = 0; c0 < n_b; c0 += kCombineMaxChunks) {
-    if (c0 > 0) {  // weights of the next pass
-      __syncthreads();
-      for (int c = c0 + tid; c < min(n_b, c0 + kCombineMaxChunks); c += 256)
-        w_lds[c - c0] = empty ? 0.0f : __builtin_amdgcn_exp2f(a.part_lse[(rec0 + c) * a.rows_per_group + rr] - M);
-      __syncthreads();
-    }
-    const int cend = min(n_b, c0 + kCombineMaxChunks);
-    int c = c0 + stream;
-    for (; c + 3 * kStreams < cend; c += 4 * kStreams) {
-      f32x4_t x[4];
+
+  // ---- running merge of this stream's chunks (a chunk with lse = -inf has weight 0)
+  float m = -__builtin_inff(), ws = 0.0f;
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int c0 = stream; c0 < n_b; c0 += kUnroll * kStreams) {
+    float lse[kUnroll];
+    f32x4_t x[kUnroll];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) x[k] = *(const f32x4_t*)(base + (int64_t)(c + k * kStreams) * rec_stride);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) acc += w_lds[c + k * kStreams - c0] * x[k];
+    for (int k = 0; k < kUnroll; ++k) {
+      const int c = c0 + k * kStreams;
+      const bool ok = c < n_b;
+      lse[k] = ok ? lse_base[(int64_t)c * a.rows_per_group] : -__builtin_inff();
+      x[k] = ok ? *(const f32x4_t*)(out_base + (int64_t)c * rec_stride) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    for (; c < cend; c += kStreams) acc += w_lds[c - c0] * *(const f32x4_t*)(base + (int64_t)c * rec_stride);
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      if (lse[k] == -__builtin_inff()) continue;
+      const float m_new = fmaxf(m, lse[k]);
+      const float sc = m == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
+      const float w = __builtin_amdgcn_exp2f(lse[k] - m_new);
+      acc = acc * sc + w * x[k];
+      ws = ws * sc + w;
+      m = m_new;
+    }
   }
 
-  // ---- phase 3: sum the streams, normalise, store
-  *(f32x4_t*)&acc_lds[stream][(tid % kThreadsPerChunk) * 4] = acc;
+  // ---- merge the streams: weights 2^(m_s - M), then column sums
+  *(f32x4_t*)&acc_lds[stream][quad * 4] = acc;
+  if (quad == 0) {
+    m_lds[stream] = m;
+    s_lds[stream] = ws;
+  }
   __syncthreads();
+  if (tid < 64) {  // one wave: lane st < kStreams holds stream st
+    const float ms = tid < kStreams ? m_lds[tid] : -__builtin_inff();
+    float M = ms;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float w = ms == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+    float total = tid < kStreams ? w * s_lds[tid] : 0.0f;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) total += __shfl_xor(total, off);
+    if (tid < kStreams) w_lds[tid] = w;
+    if (tid == 0) {
+      total_lds = total;
+      const int64_t orow = ((int64_t)b * a.seqlen_qo + s) * a.num_heads + head;
+      if (a.lse && colblk == 0) a.lse[orow] = total > 0.0f ? (M + __log2f(total)) * kLn2 : -__builtin_inff();
+    }
+  }
+  __syncthreads();
+  const float total = total_lds;
   const float inv = total > 0.0f ? 1.0f / total : 0.0f;
   const int64_t orow = ((int64_t)b * a.seqlen_qo + s) * a.num_heads + head;
   for (int cc = tid; cc < CB; cc += 256) {
     float v = 0.0f;
 #pragma unroll 8
-    for (int st = 0; st < kStreams; ++st) v += acc_lds[st][cc];
+    for (int st = 0; st < kStreams; ++st) v += w_lds[st] * acc_lds[st][cc];
     a.out[orow * kLatentDim + colblk * CB + cc] = __builtin_bit_cast(uint16_t, (__bf16)(v * inv));
   }
-  if (a.lse && colblk == 0 && tid == 0)
-    a.lse[orow] = empty ? -__builtin_inff() : (M + __log2f(total)) * kLn2;
 }
 
-template <bool FP8, int NW, int BN, int NS, int WPE, int KD, int VD>
+template <bool FP8, int HW, int KW, int NS, int WPE, int KD, int VD>
 int launch_decode_t(const DecodeArgs& a, int gx, int gy, int gz, hipStream_t st) {
-  hipLaunchKernelGGL((mla_decode_kernel<FP8, NW, BN, NS, WPE, KD, VD>), dim3(gx, gy, gz), dim3(NW * 64), 0, st, a);
+  hipLaunchKernelGGL((mla_decode_kernel<FP8, HW, KW, NS, WPE, KD, VD>), dim3(gx, gy, gz), dim3(HW * KW * 64), 0, st,
+                     a);
   return (int)hipGetLastError();
 }
 
@@ -688,20 +784,24 @@ int launch_plan(const PlanArgs& a, void* stream) {
   return (int)hipGetLastError();
 }
 
-// Tile classes: 16, 32 and 64 rows run the 64-row kernel (4 waves of one
-// 16-row head tile, one wave per SIMD, rows past the tile masked); 128 rows run
-// 8 waves (two per SIMD, 256 registers each). All on 32-row blocks, with as
-// many stages as the LDS holds.
+// Tile classes (head tiles HW x row slices KW, one wave per SIMD unless
+// noted; stages = as many blocks as the LDS holds):
+//   16 rows:  1 x 4 (fp8, 128-row blocks) or 1 x 2 (bf16, 64-row blocks)
+//   32 rows:  2 x 2 (64-row blocks)
+//   64 rows:  4 x 1 (32-row blocks)
+//   128 rows: 8 x 1 (32-row blocks, two waves per SIMD, 256 registers each)
 int launch_decode(const DecodeArgs& a, int kv_dtype, int tile_class, int gx, int gy, int gz, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const bool fp8 = kv_dtype == MLA_KV_FP8_E4M3FN;
   switch (tile_class) {
-    case 0:
-    case 1:
-    case 2: return fp8 ? launch_decode_t<true, 4, 32, 8, 1, 8, 8>(a, gx, gy, gz, st)
-                       : launch_decode_t<false, 4, 32, 4, 1, 8, 8>(a, gx, gy, gz, st);
-    case 3: return fp8 ? launch_decode_t<true, 8, 32, 8, 2, 3, 3>(a, gx, gy, gz, st)
-                       : launch_decode_t<false, 8, 32, 4, 2, 3, 3>(a, gx, gy, gz, st);
+    case 0: return fp8 ? launch_decode_t<true, 1, 4, 2, 1, 8, 8>(a, gx, gy, gz, st)
+                       : launch_decode_t<false, 1, 2, 2, 1, 8, 8>(a, gx, gy, gz, st);
+    case 1: return fp8 ? launch_decode_t<true, 2, 2, 4, 1, 8, 8>(a, gx, gy, gz, st)
+                       : launch_decode_t<false, 2, 2, 2, 1, 8, 8>(a, gx, gy, gz, st);
+    case 2: return fp8 ? launch_decode_t<true, 4, 1, 8, 1, 8, 8>(a, gx, gy, gz, st)
+                       : launch_decode_t<false, 4, 1, 4, 1, 8, 8>(a, gx, gy, gz, st);
+    case 3: return fp8 ? launch_decode_t<true, 8, 1, 8, 2, 3, 3>(a, gx, gy, gz, st)
+                       : launch_decode_t<false, 8, 1, 4, 2, 3, 3>(a, gx, gy, gz, st);
   }
   return (int)hipErrorInvalidValue;
 }

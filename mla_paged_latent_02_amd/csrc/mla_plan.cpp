@@ -64,7 +64,7 @@ const char* mla_status_string(mla_status_t s) {
 
 void mla_plan_options_default(mla_plan_options_t* out) {
   if (!out) return;
-  static const int32_t wg[4] = {4, 2, 2, 1};
+  static const int32_t wg[4] = {1, 1, 2, 1};
   static const int32_t cmin[4] = {256, 256, 256, 1024};
   static const int32_t cmax[4] = {8192, 8192, 4096, 4096};
   for (int c = 0; c < 4; ++c) {
@@ -110,7 +110,7 @@ mla_status_t mla_decode_plan_host(const mla_decode_params_t* params, const mla_p
   if (opt.force_chunk) {
     C = opt.force_chunk;
   } else {
-    int64_t want = cdiv(int64_t(num_cu) * opt.wg_per_cu[cls], B * G);
+    int64_t want = int64_t(num_cu) * opt.wg_per_cu[cls] / (B * G);
     if (want < 1) want = 1;
     C = cdiv(cdiv(L, want), mla::kBlockRows) * mla::kBlockRows;
     if (C < opt.chunk_min[cls]) C = opt.chunk_min[cls];

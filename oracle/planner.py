@@ -24,7 +24,7 @@ The rule (all integer arithmetic):
     TR   = 16 | 32 | 64 | 128          smallest of these >= rows; class = log2(TR/16)
     C    = force_chunk if set, else
            clamp(roundup(ceil(Lmax / want), 64), chunk_min[cls], chunk_max[cls])
-           with want = max(1, ceil(num_cu * wg_per_cu[cls] / (B * G)))
+           with want = max(1, floor(num_cu * wg_per_cu[cls] / (B * G)))
     max_chunks = ceil(Lmax / C)        grid = (max_chunks, G, B)
 
 Per sequence (device half): a sequence is valid when ``S <= ctx_b <= Lmax`` and
@@ -53,7 +53,7 @@ def _cdiv(a: int, b: int) -> int:
 
 @dataclass
 class PlanOptions:
-    wg_per_cu: List[int] = field(default_factory=lambda: [4, 2, 2, 1])
+    wg_per_cu: List[int] = field(default_factory=lambda: [1, 1, 2, 1])
     chunk_min: List[int] = field(default_factory=lambda: [256, 256, 256, 1024])
     chunk_max: List[int] = field(default_factory=lambda: [8192, 8192, 4096, 4096])
     force_chunk: int = 0
@@ -71,7 +71,7 @@ def reference_plan(batch, seqlen_qo, num_heads, max_context_len, num_cu, options
     if o.force_chunk:
         C = int(o.force_chunk)
     else:
-        want = max(1, _cdiv(num_cu * o.wg_per_cu[cls], B * G))
+        want = max(1, (num_cu * o.wg_per_cu[cls]) // (B * G))
         C = _cdiv(_cdiv(L, want), BLOCK_ROWS) * BLOCK_ROWS
         C = min(max(C, o.chunk_min[cls]), o.chunk_max[cls])
     max_chunks = _cdiv(L, C)

@@ -40,8 +40,14 @@ def test_plan_values_for_the_benchmark_shapes():
     assert (p["heads_per_group"], p["tile_rows"], p["chunk_len"], p["max_chunks"]) == (16, 64, 1344, 4)
     p = reference_plan(256, 1, 128, 23333, 256)
     assert (p["chunk_len"], p["max_chunks"]) == (4096, 6)
+    # 12 heads, one sequence: want = 256 -> ceil(109440 / 256) = 428 -> 448 rows, 245 chunks
     p = reference_plan(1, 1, 12, 109440, 256)
-    assert (p["tile_rows"], p["chunk_len"], p["max_chunks"]) == (16, 256, 428)
+    assert (p["tile_rows"], p["chunk_len"], p["max_chunks"]) == (16, 448, 245)
+    # five sequences: want = floor(256 / 5) = 51 -> 2146 -> 2176 rows, 51 chunks, 255 workgroups
+    # (a ceiling would give 52 -> 2112 rows -> 52 chunks, 260 workgroups on 256 CUs)
+    p = reference_plan(5, 1, 12, 109440, 256)
+    assert (p["chunk_len"], p["max_chunks"]) == (2176, 51)
+    assert 5 * p["max_chunks"] <= 256
     p = reference_plan(2, 1, 16, 100, 256, PlanOptions(force_chunk=64))
     assert (p["chunk_len"], p["max_chunks"]) == (64, 2)
 
