@@ -32,7 +32,7 @@
  *  - All pointers named d_* are device pointers (HIP device memory of the
  *    current device); everything else is host memory. The caller owns every
  *    buffer; the library never allocates or frees device memory, and never
- *    synchronises the stream (except mla_debug_read_plan_arrays).
+ *    synchronises the stream (except the mla_debug_* test hooks).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work
  *    is enqueued in call order; the library keeps no state between calls.
  *  - Host-detectable errors are returned before any device work is enqueued.
@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+#define MLA_ABI_VERSION 2
 #define MLA_ROW_DIM 576    /* q / cache row width: 512 latent + 64 rope */
 #define MLA_LATENT_DIM 512 /* V width = output width */
 #define MLA_MAX_SEQLEN_QO 8
@@ -109,13 +109,15 @@ typedef struct {
   int32_t tile_class;      /* log2(tile_rows / 16) */
   int32_t chunk_len;       /* C, cache rows per workgroup, multiple of 64 */
   int32_t max_chunks;      /* ceil(max_context_len / C) */
-  int32_t grid[3];         /* decode grid: (max_chunks, G, B) */
+  int32_t grid[3];         /* decode grid: (work_capacity * G, 1, 1) */
   int64_t partial_capacity_records; /* B * G * max_chunks */
-  uint64_t ws_status_offset;   /* uint32 status word (+ reserved), bytes from workspace start */
+  int64_t work_capacity;            /* B * max_chunks: entries of the work list */
+  uint64_t ws_status_offset;   /* uint32 [4]: status bits, work-item count, 0, 0 (bytes from workspace start) */
   uint64_t ws_nchunks_offset;  /* int32 [B]: chunks of each sequence (0 = invalid sequence) */
   uint64_t ws_partbase_offset; /* int32 [B]: first partial record of each sequence */
   uint64_t ws_part_out_offset; /* float [records][rows_per_group][512]: normalised partial outputs */
   uint64_t ws_part_lse_offset; /* float [records][rows_per_group]: partial lse, base-2 log */
+  uint64_t ws_work_offset;     /* int32 [work_capacity][2]: (sequence, chunk) work items in dispatch order */
   uint64_t ws_bytes;           /* total workspace bytes needed */
 } mla_plan_t;
 
@@ -138,7 +140,7 @@ void mla_plan_options_default(mla_plan_options_t* out);
  *   hpg = min(H, 128/S); G = ceil(H/hpg); TR = smallest of 16/32/64/128 >= hpg*S
  *   C = force_chunk or clamp(roundup(ceil(Lmax / want), 64), chunk_min, chunk_max),
  *       want = max(1, floor(num_cu * wg_per_cu / (B*G)))
- *   max_chunks = ceil(Lmax / C), grid = (max_chunks, G, B)
+ *   max_chunks = ceil(Lmax / C), work_capacity = B * max_chunks, grid = (work_capacity * G, 1, 1)
  */
 mla_status_t mla_decode_plan_host(const mla_decode_params_t* params, const mla_plan_options_t* options,
                                   int32_t num_cu, mla_plan_t* out_plan);
@@ -151,17 +153,23 @@ size_t mla_decode_workspace_size(const mla_decode_params_t* params, const mla_pl
  * Full planner: the host half above, then one device launch that, per
  * sequence, validates context_lens[b] (S <= ctx <= max_context_len, enough
  * pages), writes n_b = ceil(ctx_b / C) (0 if invalid), the exclusive prefix
- * sum of partial records, and the status word. d_context_lens [B] and
- * d_kv_indptr [B+1] are int32 device arrays. The device arrays stay valid for
- * every mla_decode / mla_split_combine call with the same context lengths.
+ * sum of partial records, the status word, and the work list: the decode
+ * workgroups' items (b, chunk) in dispatch order, longest first so that the
+ * last workgroups on the CUs are short (a scheduling choice of this library):
+ * every full chunk (exactly C rows) in (b, chunk) order; then each sequence's
+ * partial last chunk (r = ctx - (n_b - 1) C rows) by length class
+ * floor(16 r / C), longest class first, ties by b; then (b, -1) for every
+ * invalid sequence. The item count goes to status word 1. d_context_lens [B]
+ * and d_kv_indptr [B+1] are int32 device arrays. The device arrays stay valid
+ * for every mla_decode / mla_split_combine call with the same context lengths.
  */
 mla_status_t mla_decode_plan(const mla_decode_params_t* params, const mla_plan_options_t* options,
                              int32_t num_cu, const int32_t* d_context_lens, const int32_t* d_kv_indptr,
                              void* d_workspace, size_t workspace_bytes, void* stream, mla_plan_t* out_plan);
 
 /*
- * Decode attention over the paged cache. One workgroup per (chunk, head group,
- * sequence); a workgroup whose chunk is past its sequence's n_b exits at once.
+ * Decode attention over the paged cache. Workgroup x runs work item x / G for
+ * head group x % G; workgroups past the item count exit at once.
  *   d_q              bf16 [B, S, H, 576], contiguous
  *   d_kv_cache       [num_slots, 576] bf16 or fp8 e4m3fn bytes, contiguous
  *   d_kv_indptr      int32 [B+1]: page list of b is d_kv_page_indices[indptr[b] .. indptr[b+1])
@@ -195,6 +203,14 @@ mla_status_t mla_split_combine(const mla_plan_t* plan, void* d_workspace, size_t
  */
 mla_status_t mla_debug_read_plan_arrays(const mla_plan_t* plan, const void* d_workspace,
                                         int32_t* h_nchunks, int32_t* h_partbase, uint32_t* h_status);
+
+/*
+ * Test hook: synchronously copies the work list to host memory. *h_count
+ * receives the number of items; h_items (may be NULL) receives 2 * count
+ * int32, (sequence, chunk) pairs, and must hold 2 * plan->work_capacity.
+ */
+mla_status_t mla_debug_read_work_list(const mla_plan_t* plan, const void* d_workspace, int32_t* h_count,
+                                      int32_t* h_items);
 
 #ifdef __cplusplus
 }

@@ -30,7 +30,7 @@ DEV_PAGE_OUT_OF_RANGE = 8
 # Every function the header declares, in declaration order.
 EXPORTED = ["mla_abi_version", "mla_status_string", "mla_plan_options_default", "mla_decode_plan_host",
             "mla_decode_workspace_size", "mla_decode_plan", "mla_decode", "mla_split_combine",
-            "mla_debug_read_plan_arrays"]
+            "mla_debug_read_plan_arrays", "mla_debug_read_work_list"]
 
 
 class DecodeParams(ctypes.Structure):
@@ -50,9 +50,10 @@ class Plan(ctypes.Structure):
                 ("options", PlanOptions), ("heads_per_group", ctypes.c_int32), ("num_groups", ctypes.c_int32),
                 ("rows_per_group", ctypes.c_int32), ("tile_rows", ctypes.c_int32), ("tile_class", ctypes.c_int32),
                 ("chunk_len", ctypes.c_int32), ("max_chunks", ctypes.c_int32), ("grid", ctypes.c_int32 * 3),
-                ("partial_capacity_records", ctypes.c_int64), ("ws_status_offset", ctypes.c_uint64),
-                ("ws_nchunks_offset", ctypes.c_uint64), ("ws_partbase_offset", ctypes.c_uint64),
-                ("ws_part_out_offset", ctypes.c_uint64), ("ws_part_lse_offset", ctypes.c_uint64),
+                ("partial_capacity_records", ctypes.c_int64), ("work_capacity", ctypes.c_int64),
+                ("ws_status_offset", ctypes.c_uint64), ("ws_nchunks_offset", ctypes.c_uint64),
+                ("ws_partbase_offset", ctypes.c_uint64), ("ws_part_out_offset", ctypes.c_uint64),
+                ("ws_part_lse_offset", ctypes.c_uint64), ("ws_work_offset", ctypes.c_uint64),
                 ("ws_bytes", ctypes.c_uint64)]
 
 
@@ -78,6 +79,7 @@ def _load():
         "mla_decode": ([P(Plan), V, V, V, V, V, V, V, V, ctypes.c_size_t, V], ctypes.c_int),
         "mla_split_combine": ([P(Plan), V, ctypes.c_size_t, V, V, V], ctypes.c_int),
         "mla_debug_read_plan_arrays": ([P(Plan), V, V, V, V], ctypes.c_int),
+        "mla_debug_read_work_list": ([P(Plan), V, V, V], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -187,10 +189,21 @@ def read_plan_arrays(plan: Plan, workspace):
     return list(n), list(base), status.value
 
 
+def read_work_list(plan: Plan, workspace):
+    """The planner's work list, [(sequence, chunk), ...] in dispatch order, copied synchronously."""
+    count = ctypes.c_int32(0)
+    items = (ctypes.c_int32 * (2 * max(1, plan.work_capacity)))()
+    st = _lib.mla_debug_read_work_list(ctypes.byref(plan), _ptr(workspace), ctypes.cast(ctypes.byref(count), ctypes.c_void_p),
+                                       ctypes.cast(items, ctypes.c_void_p))
+    if st != MLA_OK:
+        raise MlaError("mla_debug_read_work_list", st)
+    return [(items[2 * i], items[2 * i + 1]) for i in range(count.value)]
+
+
 def plan_to_dict(plan: Plan) -> dict:
     return {
         "heads_per_group": plan.heads_per_group, "num_groups": plan.num_groups,
         "rows_per_group": plan.rows_per_group, "tile_rows": plan.tile_rows, "tile_class": plan.tile_class,
         "chunk_len": plan.chunk_len, "max_chunks": plan.max_chunks, "grid": tuple(plan.grid),
-        "partial_capacity_records": plan.partial_capacity_records,
+        "partial_capacity_records": plan.partial_capacity_records, "work_capacity": plan.work_capacity,
     }

@@ -31,6 +31,7 @@ mla_status_t mla_decode_plan(const mla_decode_params_t* params, const mla_plan_o
   a.kv_indptr = d_kv_indptr;
   a.nchunks = reinterpret_cast<int32_t*>(ws_at(d_workspace, plan.ws_nchunks_offset));
   a.partbase = reinterpret_cast<int32_t*>(ws_at(d_workspace, plan.ws_partbase_offset));
+  a.work = reinterpret_cast<int32_t*>(ws_at(d_workspace, plan.ws_work_offset));
   a.status = reinterpret_cast<uint32_t*>(ws_at(d_workspace, plan.ws_status_offset));
   a.batch = plan.params.batch;
   a.seqlen_qo = plan.params.seqlen_qo;
@@ -60,6 +61,7 @@ mla_status_t mla_decode(const mla_plan_t* plan, const void* d_q, const void* d_k
   a.context_lens = d_context_lens;
   a.nchunks = reinterpret_cast<const int32_t*>(ws_at(d_workspace, plan->ws_nchunks_offset));
   a.partbase = reinterpret_cast<const int32_t*>(ws_at(d_workspace, plan->ws_partbase_offset));
+  a.work = reinterpret_cast<const int32_t*>(ws_at(d_workspace, plan->ws_work_offset));
   a.status = reinterpret_cast<uint32_t*>(ws_at(d_workspace, plan->ws_status_offset));
   a.out = static_cast<uint16_t*>(d_out);
   a.lse = d_lse;
@@ -119,6 +121,22 @@ mla_status_t mla_debug_read_plan_arrays(const mla_plan_t* plan, const void* d_wo
   if (h_partbase && hipMemcpy(h_partbase, ws + plan->ws_partbase_offset, nb, hipMemcpyDeviceToHost) != hipSuccess)
     return MLA_ERR_HIP;
   if (h_status && hipMemcpy(h_status, ws + plan->ws_status_offset, 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+mla_status_t mla_debug_read_work_list(const mla_plan_t* plan, const void* d_workspace, int32_t* h_count,
+                                      int32_t* h_items) {
+  if (!plan_ok(plan)) return MLA_ERR_BAD_PLAN;
+  if (!d_workspace || !h_count) return MLA_ERR_INVALID_ARG;
+  const uint8_t* ws = static_cast<const uint8_t*>(d_workspace);
+  uint32_t words[2];
+  if (hipDeviceSynchronize() != hipSuccess) return MLA_ERR_HIP;
+  if (hipMemcpy(words, ws + plan->ws_status_offset, 8, hipMemcpyDeviceToHost) != hipSuccess) return MLA_ERR_HIP;
+  if (int64_t(words[1]) > plan->work_capacity) return MLA_ERR_BAD_PLAN;
+  *h_count = int32_t(words[1]);
+  if (h_items && words[1] > 0 &&
+      hipMemcpy(h_items, ws + plan->ws_work_offset, size_t(words[1]) * 8, hipMemcpyDeviceToHost) != hipSuccess)
     return MLA_ERR_HIP;
   return MLA_OK;
 }

@@ -22,7 +22,8 @@ struct DecodeArgs {
   const int32_t* context_lens;  // [B]
   const int32_t* nchunks;       // [B] from the planner
   const int32_t* partbase;      // [B] from the planner
-  uint32_t* status;             // status word
+  const int32_t* work;          // [capacity][2] (sequence, chunk) items from the planner
+  uint32_t* status;             // [0] status bits, [1] work-item count
   uint16_t* out;                // bf16 [B, S, H, 512]
   float* lse;                   // [B, S, H] or null
   float* part_out;              // [records][rows][512]
@@ -52,6 +53,7 @@ struct PlanArgs {
   const int32_t* kv_indptr;
   int32_t* nchunks;
   int32_t* partbase;
+  int32_t* work;
   uint32_t* status;
   int32_t batch, seqlen_qo, max_context_len, page_size, chunk_len, num_groups;
 };

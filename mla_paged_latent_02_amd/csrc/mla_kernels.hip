@@ -89,42 +89,126 @@ __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
 }
 
 // ---------------------------------------------------------------------------
-// Planner: one workgroup walks the batch in tiles of 256 sequences.
+// Planner: one workgroup walks the batch in tiles of 256 sequences, twice.
+// Pass 1 counts the work items of each kind; pass 2 writes the per-sequence
+// arrays and places every item of the work list: full chunks in (sequence,
+// chunk) order, then partial last chunks by length class (longest first,
+// ties by sequence), then one NaN-fill item per invalid sequence. Ranks
+// within a class follow sequence order (wave ballots plus per-wave counts),
+// so the list is deterministic.
+constexpr int kLengthClasses = 16;
+constexpr int kCats = kLengthClasses + 1;  // length classes, then invalid sequences
+
+struct SeqWork {
+  int32_t n;      // chunks (0: invalid sequence)
+  int32_t nfull;  // chunks of exactly chunk_len rows
+  int32_t cat;    // -1: none; 0..15: length class of the partial last chunk; 16: invalid
+  uint32_t bad;   // status bits
+};
+
+__device__ __forceinline__ SeqWork seq_work(const PlanArgs& a, int b) {
+  SeqWork w{0, 0, -1, 0u};
+  if (b >= a.batch) return w;
+  const int32_t ctx = a.context_lens[b];
+  const int32_t pages = a.kv_indptr[b + 1] - a.kv_indptr[b];
+  if (ctx < a.seqlen_qo) w.bad |= MLA_DEV_CTX_TOO_SHORT;
+  if (ctx > a.max_context_len) w.bad |= MLA_DEV_CTX_TOO_LONG;
+  if (!w.bad && (int64_t)pages * a.page_size < (int64_t)ctx) w.bad |= MLA_DEV_TOO_FEW_PAGES;
+  if (w.bad) {
+    w.cat = kLengthClasses;
+    return w;
+  }
+  const int32_t C = a.chunk_len;
+  w.n = (ctx + C - 1) / C;
+  const int32_t last = ctx - (w.n - 1) * C;  // 1..C
+  w.nfull = last == C ? w.n : w.n - 1;
+  if (last < C) w.cat = (int32_t)((int64_t)kLengthClasses * last / C);
+  return w;
+}
+
 __global__ __launch_bounds__(256) void mla_plan_kernel(PlanArgs a) {
-  __shared__ int32_t scan[256];
+  __shared__ int32_t scan_pb[256], scan_full[256];
+  __shared__ int32_t cat_wave[4][kCats];
+  __shared__ int32_t cat_total[kCats], cat_base[kCats], cat_carry[kCats];
+  __shared__ int32_t full_total;
   __shared__ uint32_t bad_or[256];
   const int tid = threadIdx.x;
-  int32_t carry = 0;
+  const int lane = tid & 63, wave = tid >> 6;
+
+  // ---- pass 1: totals of each kind of item
+  if (tid < kCats) {
+    cat_total[tid] = 0;
+    cat_carry[tid] = 0;
+  }
+  if (tid == 0) full_total = 0;
+  __syncthreads();
   uint32_t bad_acc = 0;
+  int32_t my_full = 0;
+  for (int base = 0; base < a.batch; base += 256) {
+    const SeqWork w = seq_work(a, base + tid);
+    bad_acc |= w.bad;
+    my_full += w.nfull;
+    if (w.cat >= 0) atomicAdd(&cat_total[w.cat], 1);
+  }
+  atomicAdd(&full_total, my_full);
+  __syncthreads();
+  if (tid == 0) {
+    int32_t pos = full_total;
+    for (int k = kLengthClasses - 1; k >= 0; --k) {
+      cat_base[k] = pos;
+      pos += cat_total[k];
+    }
+    cat_base[kLengthClasses] = pos;
+    pos += cat_total[kLengthClasses];
+    a.status[1] = (uint32_t)pos;  // work items
+  }
+  __syncthreads();
+
+  // ---- pass 2: per-sequence arrays and the work list
+  int32_t carry_pb = 0, carry_full = 0;
   for (int base = 0; base < a.batch; base += 256) {
     const int b = base + tid;
-    int32_t n = 0, contrib = 0;
-    if (b < a.batch) {
-      const int32_t ctx = a.context_lens[b];
-      const int32_t pages = a.kv_indptr[b + 1] - a.kv_indptr[b];
-      uint32_t bad = 0;
-      if (ctx < a.seqlen_qo) bad |= MLA_DEV_CTX_TOO_SHORT;
-      if (ctx > a.max_context_len) bad |= MLA_DEV_CTX_TOO_LONG;
-      if (!bad && (int64_t)pages * a.page_size < (int64_t)ctx) bad |= MLA_DEV_TOO_FEW_PAGES;
-      bad_acc |= bad;
-      n = bad ? 0 : (ctx + a.chunk_len - 1) / a.chunk_len;
-      contrib = (n > 1 ? n : 0) * a.num_groups;
+    const SeqWork w = seq_work(a, b);
+    const int32_t contrib = (w.n > 1 ? w.n : 0) * a.num_groups;
+    scan_pb[tid] = contrib;
+    scan_full[tid] = w.nfull;
+    int32_t rank = 0;  // among the earlier sequences of this wave with the same class
+    for (int k = 0; k < kCats; ++k) {
+      const uint64_t m = __builtin_amdgcn_ballot_w64(w.cat == k);
+      if (w.cat == k) rank = __popcll(m & ((1ull << lane) - 1));
+      if (lane == 0) cat_wave[wave][k] = __popcll(m);
     }
-    scan[tid] = contrib;
     __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {  // inclusive Hillis-Steele scan
-      int32_t v = tid >= off ? scan[tid - off] : 0;
+    for (int off = 1; off < 256; off <<= 1) {  // inclusive Hillis-Steele scans
+      const int32_t v0 = tid >= off ? scan_pb[tid - off] : 0;
+      const int32_t v1 = tid >= off ? scan_full[tid - off] : 0;
       __syncthreads();
-      scan[tid] += v;
+      scan_pb[tid] += v0;
+      scan_full[tid] += v1;
       __syncthreads();
     }
     if (b < a.batch) {
-      a.nchunks[b] = n;
-      a.partbase[b] = carry + scan[tid] - contrib;
+      a.nchunks[b] = w.n;
+      a.partbase[b] = carry_pb + scan_pb[tid] - contrib;
+      const int32_t p0 = carry_full + scan_full[tid] - w.nfull;
+      for (int c = 0; c < w.nfull; ++c) {
+        a.work[2 * (p0 + c)] = b;
+        a.work[2 * (p0 + c) + 1] = c;
+      }
+      if (w.cat >= 0) {
+        int32_t pos = cat_base[w.cat] + cat_carry[w.cat] + rank;
+        for (int v = 0; v < wave; ++v) pos += cat_wave[v][w.cat];
+        a.work[2 * pos] = b;
+        a.work[2 * pos + 1] = w.cat == kLengthClasses ? -1 : w.n - 1;
+      }
     }
-    carry += scan[255];
+    carry_pb += scan_pb[255];
+    carry_full += scan_full[255];
+    __syncthreads();
+    if (tid < kCats) cat_carry[tid] += cat_wave[0][tid] + cat_wave[1][tid] + cat_wave[2][tid] + cat_wave[3][tid];
     __syncthreads();
   }
+
   bad_or[tid] = bad_acc;
   __syncthreads();
   for (int off = 128; off > 0; off >>= 1) {
@@ -133,22 +217,13 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(PlanArgs a) {
   }
   if (tid == 0) {
     a.status[0] = bad_or[0];
-    a.status[1] = 0;
     a.status[2] = 0;
     a.status[3] = 0;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Decode. One workgroup = one (chunk, head group, sequence) with HW x KW
-// waves. Wave (hw, kw) owns head tile hw (16 tile rows: its query fragments
-// and its 16 x 512 fp32 output stay in registers for the whole chunk) and
-// cache rows [32 kw, 32 kw + 32) of every block of BN = 32 KW rows, with its
-// own online-softmax state. The KW states of a head tile are merged through
-// LDS at the end of the chunk. All waves load each block into an LDS ring of
-// NS stages; a block's rows are gathered by every wave together.
-//
-// LDS block layout (one stage, BN cache rows):
+// LDS block layout (one ring stage, BN cache rows):
 //   main region: row r at r*kMainStride holds the 512 latent elements (the V
 //                part); the stride is padded by 16 bytes so that consecutive
 //                rows start on different banks;
@@ -171,26 +246,6 @@ struct RowLayout {
   static constexpr int kBlockBytes = kTailBase + BN * kTailBytes;
   // the tail row stride spans kTailBytes/4 banks; the row bits above that pick the xor
   static __device__ __forceinline__ int tail_xor(int r) { return FP8 ? ((r >> 2) & 3) : ((r >> 1) & 7); }
-};
-
-template <bool FP8, int HW, int KW, int NS>
-struct DecodeCfg {
-  static constexpr int kWaves = HW * KW;
-  static constexpr int kBlockN = 32 * KW;  // cache rows per block
-  using L = RowLayout<FP8, kBlockN>;
-  static constexpr int kRingBytes = NS * L::kBlockBytes;
-  // merge area after the loop: every wave's 16 x 512 fp32 output, then its max and sum per head
-  static constexpr int kMergeBytes = KW > 1 ? kWaves * (32 * 64 * 16 + 2 * 16 * 4) : 0;
-  static constexpr int kLdsBytes = kRingBytes > kMergeBytes ? kRingBytes : kMergeBytes;
-  static constexpr int kRowsPerWave = kBlockN / kWaves;  // rows each wave gathers per block
-  static constexpr int kTailRowsPerInst = 64 / L::kTailSlots;
-  static constexpr int kTailInsts = (kRowsPerWave + kTailRowsPerInst - 1) / kTailRowsPerInst;
-  static constexpr int kDmaInsts = kRowsPerWave + kTailInsts;  // vector-memory instructions per wave per block
-  static constexpr int kTiles = 2;                             // score tiles of 16 rows per wave per block
-  static constexpr int kKSteps = 1;                            // PV k-steps of 32 rows per wave per block
-  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-  static_assert(kRowsPerWave >= 1 && kBlockN % kWaves == 0, "row split");
-  static_assert((NS - 2) * kDmaInsts <= 63, "vmcnt range");
 };
 
 __device__ __forceinline__ u32x4_t lds_b128(LDS_PTR(uint8_t) base, uint32_t off) {
@@ -232,24 +287,282 @@ __device__ __forceinline__ int perm_row(int m, int odd) {
   return (2 * r + 8 * (g & 1) + (g >> 1)) ^ odd;
 }
 
-template <bool FP8, int HW, int KW, int NS, int WPE, int KD, int VD>
+// Page-gathered loads of one chunk's cache rows, in blocks of BN rows, into
+// an LDS ring of NS stages; the NW waves of the workgroup gather every block
+// together. Row r of wave w's share of block blk is cache row
+// min(c_start + blk*BN + w*RPW + r, c_end - 1): rows past the chunk repeat its
+// last row, whose scores are masked. Protocol, per block blk of the loop:
+//   wait(blk); __syncthreads(); advance(blk); ... read stage blk % NS ...
+// The page ids come either
+//  - (ring of more than two stages) from scalar loads, so that the only
+//    vector-memory instructions in the loop are the kDmaInsts DMA
+//    instructions per block and the ring can wait for its oldest block alone;
+//  - (two stages) from one vector load per block (lane r: row r), issued
+//    right after the previous block's DMA: the loop waits for all its loads
+//    at the top anyway, and no scalar register has to hold a block of ids.
+// A page id outside the pool is replaced by page 0 and noted in bad_page.
+template <bool FP8, int NW, int BN, int NS>
+struct BlockGather {
+  using L = RowLayout<FP8, BN>;
+  static constexpr int RPW = BN / NW;  // rows each wave gathers per block
+  static constexpr int kTailRowsPerInst = 64 / L::kTailSlots;
+  static constexpr int kTailInsts = (RPW + kTailRowsPerInst - 1) / kTailRowsPerInst;
+  static constexpr int kDmaInsts = RPW + kTailInsts;  // vector-memory instructions per wave per block
+  static constexpr bool kVecPages = NS == 2;
+  static_assert(RPW >= 1 && BN % NW == 0, "row split");
+  static_assert((NS - 2) * kDmaInsts <= 63, "vmcnt range");
+
+  const uint8_t* cache;
+  const int32_t* page_ids;
+  const __attribute__((address_space(4))) int32_t* page_ids_s;
+  int64_t num_pages;
+  uint32_t magic, lds_base;
+  int c_start, c_end, nblk, page_base, P, wave, lane, tslot, trow, my_row;
+  bool bad_page;
+  int v_page;                       // two stages: lane r < RPW holds the page id of row r of the next block
+  int page_n[kVecPages ? 1 : RPW];  // more stages: page ids of the next block
+
+  __device__ __forceinline__ BlockGather(const DecodeArgs& a, uint32_t lds_base_, int c_start_, int c_end_,
+                                         int page_base_, int wave_, int lane_)
+      : cache(a.cache),
+        page_ids(a.kv_page_indices),
+        page_ids_s((const __attribute__((address_space(4))) int32_t*)a.kv_page_indices),
+        num_pages(a.num_pages),
+        magic(a.page_div_magic),
+        lds_base(lds_base_),
+        c_start(c_start_),
+        c_end(c_end_),
+        nblk((c_end_ - c_start_ + BN - 1) / BN),
+        page_base(page_base_),
+        P(a.page_size),
+        wave(wave_),
+        lane(lane_),
+        tslot(lane_ % L::kTailSlots),
+        trow(lane_ / L::kTailSlots),
+        my_row(lane_ < RPW ? lane_ : RPW - 1),
+        bad_page(false),
+        v_page(0) {}
+
+  __device__ __forceinline__ void page_pos(int kv, int& q, int& rem) const {
+    q = (int)__umulhi((uint32_t)kv, magic);
+    rem = kv - q * P;
+    if (rem >= P) {
+      ++q;
+      rem -= P;
+    }
+  }
+  __device__ __forceinline__ int row_kv(int blk, int r) const {
+    return min(c_start + blk * BN + wave * RPW + r, c_end - 1);
+  }
+  __device__ __forceinline__ int checked(int pg) {
+    if ((uint32_t)pg >= (uint64_t)num_pages) {
+      bad_page = true;
+      pg = 0;
+    }
+    return pg;
+  }
+  // main part of row r: one instruction; lane l fetches the row's 16-byte slot l
+  // (bf16: 64 slots; fp8: 32 slots, upper half of the wave idle)
+  __device__ __forceinline__ void issue_main_row(int blk, int r, int slot_s) const {
+    const uint32_t stage_off = (uint32_t)(blk % NS) * L::kBlockBytes;
+    const uint8_t* src = cache + (int64_t)slot_s * L::kRowBytes + (lane << 4);
+    const uint32_t dst =
+        __builtin_amdgcn_readfirstlane(lds_base + stage_off + (uint32_t)((wave * RPW + r) * L::kMainStride));
+    if (FP8 ? lane < 32 : true) dma16(src, dst);
+  }
+  // rope tails: instruction m covers kTailRowsPerInst rows x kTailSlots slots;
+  // sv is the slot of this lane's row
+  __device__ __forceinline__ void issue_tail(int blk, int m, int sv) const {
+    const uint32_t stage_off = (uint32_t)(blk % NS) * L::kBlockBytes;
+    const int r = wave * RPW + m * kTailRowsPerInst + trow;
+    const int logical = tslot ^ L::tail_xor(r);
+    const uint8_t* src = cache + (int64_t)sv * L::kRowBytes + L::kMainBytes + (logical << 4);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(
+        lds_base + stage_off + (uint32_t)(L::kTailBase + (wave * RPW + m * kTailRowsPerInst) * L::kTailBytes));
+    if (m * kTailRowsPerInst + trow < RPW) dma16(src, dst);
+  }
+  __device__ __forceinline__ void fetch(int blk) {
+    if constexpr (kVecPages) {
+      int q, rem;
+      page_pos(row_kv(blk, my_row), q, rem);
+      v_page = page_ids[page_base + q];
+    } else {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        int q, rem;
+        page_pos(__builtin_amdgcn_readfirstlane(row_kv(blk, r)), q, rem);
+        page_n[r] = page_ids_s[page_base + q];
+      }
+    }
+  }
+  __device__ __forceinline__ void issue(int blk) {
+    if constexpr (kVecPages) {
+      int q, rem;
+      page_pos(row_kv(blk, my_row), q, rem);
+      const int slot_v = checked(v_page) * P + rem;
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) issue_main_row(blk, r, __builtin_amdgcn_readlane(slot_v, r));
+#pragma unroll
+      for (int m = 0; m < kTailInsts; ++m)
+        issue_tail(blk, m, __builtin_amdgcn_ds_bpermute((m * kTailRowsPerInst + trow) << 2, slot_v));
+    } else {
+      int slot[RPW];
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        int q, rem;
+        page_pos(__builtin_amdgcn_readfirstlane(row_kv(blk, r)), q, rem);
+        slot[r] = checked(page_n[r]) * P + rem;
+        issue_main_row(blk, r, slot[r]);
+      }
+#pragma unroll
+      for (int m = 0; m < kTailInsts; ++m) {
+        int sv = slot[m * kTailRowsPerInst];
+#pragma unroll
+        for (int k = 1; k < kTailRowsPerInst; ++k)
+          if (m * kTailRowsPerInst + k < RPW && trow == k) sv = slot[m * kTailRowsPerInst + k];
+        issue_tail(blk, m, sv);
+      }
+    }
+  }
+  // prologue: blocks 0 .. NS-2 in flight, page ids of block NS-1 fetched
+  __device__ __forceinline__ void start() {
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i) {
+      if (i < nblk) {
+        fetch(i);
+        issue(i);
+      }
+    }
+    if (NS - 1 < nblk) fetch(NS - 1);
+  }
+  // this wave's loads of block blk have landed (the caller then synchronises the workgroup)
+  __device__ __forceinline__ void wait(int blk) const {
+    // blocks issued after blk so far: blk+1 .. min(blk+NS-2, nblk-1)
+    wait_vmcnt_blocks<kDmaInsts, NS - 2>(nblk - 1 - blk);
+  }
+  // after the barrier that publishes block blk: the stage of block blk-1 is free
+  __device__ __forceinline__ void advance(int blk) {
+    if (blk + NS - 1 < nblk) {
+      issue(blk + NS - 1);
+      if (blk + NS < nblk) fetch(blk + NS);
+    }
+  }
+  __device__ __forceinline__ void report(uint32_t* status) const {
+    if (__builtin_amdgcn_ballot_w64(bad_page) && lane == 0) atomicOr(status, MLA_DEV_PAGE_OUT_OF_RANGE);
+  }
+};
+
+// Rows of an invalid sequence (n_b == 0) are NaN, written by its work item.
+__device__ __forceinline__ void fill_invalid_rows(const DecodeArgs& a, int b, int grp, int wave, int nwaves,
+                                                  int lane) {
+  const float nan = __builtin_nanf("");
+  for (int rr = wave; rr < a.rows_per_group; rr += nwaves) {
+    const int s = rr / a.heads_per_group;
+    const int head = grp * a.heads_per_group + rr % a.heads_per_group;
+    if (head >= a.num_heads) continue;
+    const int64_t row = ((int64_t)b * a.seqlen_qo + s) * a.num_heads + head;
+    for (int c = lane; c < kLatentDim; c += 64) a.out[row * kLatentDim + c] = 0x7fc0;
+    if (a.lse && lane == 0) a.lse[row] = nan;
+  }
+}
+
+// Tile row rr of head group grp: its output row, its visible end in the chunk
+// (the causal mask lets token s see ctx - S + 1 + s rows) and whether it exists.
+__device__ __forceinline__ void tile_row(const DecodeArgs& a, int b, int grp, int rr, int ctx, int c_end,
+                                         int& vis_end, int& row_out, bool& row_ok) {
+  const int tok = rr / a.heads_per_group;
+  const int head = grp * a.heads_per_group + rr % a.heads_per_group;
+  row_ok = rr < a.rows_per_group && head < a.num_heads;
+  vis_end = min(c_end, a.causal ? ctx - a.seqlen_qo + 1 + tok : ctx);
+  row_out = row_ok ? (int)(((int64_t)b * a.seqlen_qo + tok) * a.num_heads + head) : 0;
+}
+
+// One head tile's online softmax over a block of 32 cache rows (two score tiles
+// of S^T, lane = one head row, 4 rows per tile per lane): masks rows at or past
+// vis_end, moves the reference max lazily, accumulates the row sum and returns
+// P^T as one bf16 MFMA operand plus the factor for the output accumulator.
+// pg: score row 4*g4 + r of a tile is cache row 2r + (pg ^ (tile & 1)).
+__device__ __forceinline__ bf16x8_t softmax_block(f32x4_t (&s)[2], float sscale, int lim0, int lim1, float& m_ref,
+                                                  float& l_part, float& alpha, bool& up) {
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v = s[nt][r] * sscale;
+      v = nt * 16 + 2 * r < (nt ? lim1 : lim0) ? v : -__builtin_inff();
+      s[nt][r] = v;
+      mx = fmaxf(mx, v);
+    }
+  mx = wave_max_16x4(mx);
+  const float old = m_ref;
+  up = mx > old + kRescaleSlack;
+  const float m_new = up ? mx : old;
+  alpha = up ? __builtin_amdgcn_exp2f(old - m_new) : 1.0f;  // old = -inf gives 0
+  m_ref = m_new;
+  const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;
+  float psum = 0.0f;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = __builtin_amdgcn_exp2f(s[nt][r] - m_use);
+      s[nt][r] = p;
+      psum += p;
+    }
+  l_part = l_part * alpha + psum;
+  u32x4_t w;
+  w[0] = pack_bf16x2(s[0][0], s[0][1]);
+  w[1] = pack_bf16x2(s[0][2], s[0][3]);
+  w[2] = pack_bf16x2(s[1][0], s[1][1]);
+  w[3] = pack_bf16x2(s[1][2], s[1][3]);
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+
+// Final bf16 row (single chunk) or fp32 partial record of 4 latent columns
+// [col, col + 4) of one tile row, already divided by the row sum.
+__device__ __forceinline__ void store_out4(const DecodeArgs& a, bool final_row, int row_out, int64_t prec_row,
+                                           int col, f32x4_t o) {
+  if (final_row) {
+    u32x2_t w;
+    w[0] = pack_bf16x2(o[0], o[1]);
+    w[1] = pack_bf16x2(o[2], o[3]);
+    *(u32x2_t*)(a.out + (int64_t)row_out * kLatentDim + col) = w;
+  } else {
+    *(f32x4_t*)(a.part_out + prec_row * kLatentDim + col) = o;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode, row-split form. One workgroup = one (chunk, head group, sequence)
+// with HW x KW waves. Wave (hw, kw) owns head tile hw (16 tile rows: its query
+// fragments and its 16 x 512 fp32 output stay in registers for the whole
+// chunk) and cache rows [32 kw, 32 kw + 32) of every block of BN = 32 KW rows,
+// with its own online-softmax state. The KW states of a head tile are merged
+// through LDS at the end of the chunk.
+template <bool FP8, int HW, int KW, int NS>
+struct DecodeCfg {
+  static constexpr int kWaves = HW * KW;
+  static constexpr int kBlockN = 32 * KW;  // cache rows per block
+  using Gather = BlockGather<FP8, kWaves, kBlockN, NS>;
+  using L = typename Gather::L;
+  static constexpr int kRingBytes = NS * L::kBlockBytes;
+  // merge area after the loop: every wave's 16 x 512 fp32 output, then its max and sum per head
+  static constexpr int kMergeBytes = KW > 1 ? kWaves * (32 * 64 * 16 + 2 * 16 * 4) : 0;
+  static constexpr int kLdsBytes = kRingBytes > kMergeBytes ? kRingBytes : kMergeBytes;
+  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+};
+
+template <bool FP8, int HW, int KW, int NS, int WPE, int KD, int VD, int QC>
 __global__ __launch_bounds__(HW * KW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void mla_decode_kernel(DecodeArgs a) {
   using Cfg = DecodeCfg<FP8, HW, KW, NS>;
   using L = typename Cfg::L;
   constexpr int NW = Cfg::kWaves;
   constexpr int BN = Cfg::kBlockN;
-  constexpr int RPW = Cfg::kRowsPerWave;
-  constexpr int NT = Cfg::kTiles;
-  constexpr int NU = Cfg::kKSteps;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::kLdsBytes];
   LDS_PTR(uint8_t) lds = (LDS_PTR(uint8_t))smem;
-  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
-  const int chunk = blockIdx.x;
-  const int grp = blockIdx.y;
-  const int b = blockIdx.z;
-  const int n_b = a.nchunks[b];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keep it scalar
   const int hw = wave % HW;   // head tile
@@ -257,40 +570,24 @@ void mla_decode_kernel(DecodeArgs a) {
   const int i16 = lane & 15;  // MFMA column: head row within the wave's 16-row tile
   const int g4 = lane >> 4;   // MFMA k-group
 
-  if (chunk >= n_b) {
-    // Early-exit guard. An invalid sequence (n_b == 0) gets NaN rows from chunk 0.
-    if (n_b == 0 && chunk == 0) {
-      const float nan = __builtin_nanf("");
-      for (int rr = wave; rr < a.rows_per_group; rr += NW) {
-        const int s = rr / a.heads_per_group;
-        const int head = grp * a.heads_per_group + rr % a.heads_per_group;
-        if (head >= a.num_heads) continue;
-        const int64_t row = ((int64_t)b * a.seqlen_qo + s) * a.num_heads + head;
-        for (int c = lane; c < kLatentDim; c += 64) a.out[row * kLatentDim + c] = 0x7fc0;
-        if (a.lse && lane == 0) a.lse[row] = nan;
-      }
-    }
+  // ---- work item: workgroup x runs item x / G of the planner's list for head group x % G
+  const int item = (int)(blockIdx.x / (unsigned)a.num_groups);
+  const int grp = (int)blockIdx.x - item * a.num_groups;
+  if (item >= (int)a.status[1]) return;  // past the list
+  const int b = a.work[2 * item];
+  const int chunk = a.work[2 * item + 1];
+  if (chunk < 0) {  // invalid sequence: NaN rows
+    fill_invalid_rows(a, b, grp, wave, NW, lane);
     return;
   }
+  const int n_b = a.nchunks[b];
 
   const int ctx = a.context_lens[b];
   const int c_start = chunk * a.chunk_len;
   const int c_end = min(c_start + a.chunk_len, ctx);
-  const int nblk = (c_end - c_start + BN - 1) / BN;
-  const int page_base = a.kv_indptr[b];
-  const int P = a.page_size;
-
-  // ---- this lane's tile row and its visible limit
   int vis_end, row_out;
   bool row_ok;
-  {
-    const int rr = hw * 16 + i16;
-    const int tok = rr / a.heads_per_group;
-    const int head = grp * a.heads_per_group + rr % a.heads_per_group;
-    row_ok = rr < a.rows_per_group && head < a.num_heads;
-    vis_end = min(c_end, a.causal ? ctx - a.seqlen_qo + 1 + tok : ctx);
-    row_out = row_ok ? (int)(((int64_t)b * a.seqlen_qo + tok) * a.num_heads + head) : 0;
-  }
+  tile_row(a, b, grp, hw * 16 + i16, ctx, c_end, vis_end, row_out, row_ok);
 
   // ---- query fragments (B operand of S^T = K Q^T), resident for the whole chunk.
   // bf16 cache: fragment t holds d = 32t + 8*g4 .. +7.
@@ -313,118 +610,16 @@ void mla_decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int nt = 0; nt < 32; ++nt) o_acc[nt] = f32x4_t{0, 0, 0, 0};
 
-  // ---- page-gathered block loads.
-  // Row r of the wave's share of block blk is cache row
-  // min(c_start + blk*BN + wave*RPW + r, c_end - 1): rows past the chunk repeat
-  // its last row, whose scores are masked. The page ids come either
-  //  - (ring of more than two stages) from scalar loads, so that the only
-  //    vector-memory instructions in the loop are the Cfg::kDmaInsts DMA
-  //    instructions per block and the ring can wait for its oldest block alone;
-  //  - (two stages) from one vector load per block (lane r: row r), issued
-  //    right after the previous block's DMA: the loop waits for all its loads
-  //    at the top anyway, and no scalar register has to hold a block of ids.
-  constexpr bool kVecPages = NS == 2;
-  const uint32_t magic = a.page_div_magic;
-  const uint8_t* cache = a.cache;
-  bool bad_page = false;
-  auto page_pos = [&](int kv, int& q, int& rem) {
-    q = (int)__umulhi((uint32_t)kv, magic);
-    rem = kv - q * P;
-    if (rem >= P) {
-      ++q;
-      rem -= P;
-    }
-  };
-  auto row_kv = [&](int blk, int r) { return min(c_start + blk * BN + wave * RPW + r, c_end - 1); };
-  const int tslot = lane % L::kTailSlots;
-  const int trow = lane / L::kTailSlots;
-  // main part of row r: one instruction; lane l fetches the row's 16-byte slot l
-  // (bf16: 64 slots; fp8: 32 slots, upper half of the wave idle)
-  auto issue_main_row = [&](int blk, int r, int slot_s) {
-    const uint32_t stage_off = (uint32_t)(blk % NS) * L::kBlockBytes;
-    const uint8_t* src = cache + (int64_t)slot_s * L::kRowBytes + (lane << 4);
-    const uint32_t dst =
-        __builtin_amdgcn_readfirstlane(lds_base + stage_off + (uint32_t)((wave * RPW + r) * L::kMainStride));
-    if (FP8 ? lane < 32 : true) dma16(src, dst);
-  };
-  // rope tails: instruction m covers kTailRowsPerInst rows x kTailSlots slots;
-  // sv is the slot of this lane's row
-  auto issue_tail = [&](int blk, int m, int sv) {
-    const uint32_t stage_off = (uint32_t)(blk % NS) * L::kBlockBytes;
-    const int r = wave * RPW + m * Cfg::kTailRowsPerInst + trow;
-    const int logical = tslot ^ L::tail_xor(r);
-    const uint8_t* src = cache + (int64_t)sv * L::kRowBytes + L::kMainBytes + (logical << 4);
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(
-        lds_base + stage_off + (uint32_t)(L::kTailBase + (wave * RPW + m * Cfg::kTailRowsPerInst) * L::kTailBytes));
-    if (m * Cfg::kTailRowsPerInst + trow < RPW) dma16(src, dst);
-  };
-
-  // scalar page ids
-  const __attribute__((address_space(4))) int32_t* page_ids =
-      (const __attribute__((address_space(4))) int32_t*)a.kv_page_indices;
-  auto fetch_pages = [&](int blk, int (&page)[RPW]) {
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      int q, rem;
-      page_pos(__builtin_amdgcn_readfirstlane(row_kv(blk, r)), q, rem);
-      page[r] = page_ids[page_base + q];
-    }
-  };
-  auto issue_block = [&](int blk, const int (&page)[RPW]) {
-    int slot[RPW];
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      int q, rem;
-      page_pos(__builtin_amdgcn_readfirstlane(row_kv(blk, r)), q, rem);
-      int pg = page[r];
-      if ((uint32_t)pg >= (uint64_t)a.num_pages) {
-        bad_page = true;
-        pg = 0;
-      }
-      slot[r] = pg * P + rem;
-      issue_main_row(blk, r, slot[r]);
-    }
-#pragma unroll
-    for (int m = 0; m < Cfg::kTailInsts; ++m) {
-      int sv = slot[m * Cfg::kTailRowsPerInst];
-#pragma unroll
-      for (int k = 1; k < Cfg::kTailRowsPerInst; ++k)
-        if (m * Cfg::kTailRowsPerInst + k < RPW && trow == k) sv = slot[m * Cfg::kTailRowsPerInst + k];
-      issue_tail(blk, m, sv);
-    }
-  };
-
-  // vector page ids: lane r < RPW holds the page id of row r of the next block
-  int v_page = 0;
-  const int my_row = lane < RPW ? lane : RPW - 1;
-  auto fetch_pages_v = [&](int blk) {
-    int q, rem;
-    page_pos(row_kv(blk, my_row), q, rem);
-    v_page = a.kv_page_indices[page_base + q];
-  };
-  auto issue_block_v = [&](int blk) {
-    int q, rem;
-    page_pos(row_kv(blk, my_row), q, rem);
-    int pg = v_page;
-    if ((uint32_t)pg >= (uint64_t)a.num_pages) {
-      bad_page = true;
-      pg = 0;
-    }
-    const int slot_v = pg * P + rem;
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) issue_main_row(blk, r, __builtin_amdgcn_readlane(slot_v, r));
-#pragma unroll
-    for (int m = 0; m < Cfg::kTailInsts; ++m)
-      issue_tail(blk, m, __builtin_amdgcn_ds_bpermute((m * Cfg::kTailRowsPerInst + trow) << 2, slot_v));
-  };
+  typename Cfg::Gather gather(a, (uint32_t)(uintptr_t)lds, c_start, c_end, a.kv_indptr[b], wave, lane);
+  const int nblk = gather.nblk;
 
   // Per-lane LDS offsets that do not change over the loop; each access adds a
   // compile-time immediate. Index [o] is for tiles with nt & 1 == o.
   uint32_t k_main_base[2];
 #pragma unroll
   for (int o = 0; o < 2; ++o) k_main_base[o] = (uint32_t)perm_row(i16, o) * L::kMainStride + (uint32_t)g4 * 16;
-  // V^T reads of P^T fragment u: element e < 4 is kv row 32u + pi_0(4g4 + e),
-  // e >= 4 is 32u + 16 + pi_1(4g4 + e - 4).
+  // V^T reads of the P^T fragment: element e < 4 is kv row pi_0(4g4 + e),
+  // e >= 4 is 16 + pi_1(4g4 + e - 4).
   uint32_t v_base_lo, v_base_hi;
   if constexpr (FP8) {
     // supplier lane (k = i16/2, c = i16%2) reads element k's row, bytes 8c of the column tile
@@ -439,57 +634,37 @@ void mla_decode_kernel(DecodeArgs a) {
     v_base_hi = (uint32_t)(16 + perm_row(4 * g4 + k, 1)) * L::kMainStride + 8u * c;
   }
 
-  // ---- prologue: blocks 0 .. NS-2 in flight, pages of block NS-1 fetched
-  int page_n[kVecPages ? 1 : RPW];
-  if constexpr (kVecPages) {
-    fetch_pages_v(0);
-    issue_block_v(0);
-    if (1 < nblk) fetch_pages_v(1);
-  } else {
-#pragma unroll
-    for (int i = 0; i < NS - 1; ++i) {
-      if (i < nblk) {
-        fetch_pages(i, page_n);
-        issue_block(i, page_n);
-      }
-    }
-    if (NS - 1 < nblk) fetch_pages(NS - 1, page_n);
-  }
-
+  gather.start();
   const float sscale = a.score_scale_log2;
   const int pg = 8 * (g4 & 1) + (g4 >> 1);  // score row 4g4+r of a tile is cache row 2r + (pg ^ (nt&1))
 
   for (int blk = 0; blk < nblk; ++blk) {
-    // blocks issued after this one so far: blk+1 .. min(blk+NS-2, nblk-1)
-    wait_vmcnt_blocks<Cfg::kDmaInsts, NS - 2>(nblk - 1 - blk);
+    gather.wait(blk);
     __syncthreads();
-    if (blk + NS - 1 < nblk) {
-      if constexpr (kVecPages) {
-        issue_block_v(blk + 1);
-        if (blk + 2 < nblk) fetch_pages_v(blk + 2);
-      } else {
-        issue_block(blk + NS - 1, page_n);
-        if (blk + NS < nblk) fetch_pages(blk + NS, page_n);
-      }
-    }
+    gather.advance(blk);
     LDS_PTR(uint8_t) stage = lds + (uint32_t)(blk % NS) * L::kBlockBytes;
     // this wave's 32 rows of the block: main rows at mstage, rope tails at tstage
     LDS_PTR(uint8_t) mstage = stage + (uint32_t)(kw * 32 * L::kMainStride);
     LDS_PTR(uint8_t) tstage = stage + (uint32_t)(L::kTailBase + kw * 32 * L::kTailBytes);
     const int kv0 = c_start + blk * BN + kw * 32;
 
-    // ---- S^T[kv, head] = K Q^T for the wave's 32 rows of the block (NT tiles of 16 kv rows).
-    // The reads walk (step, tile) with a ring of KD reads in flight.
-    f32x4_t sacc[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) sacc[nt] = f32x4_t{0, 0, 0, 0};
+    // ---- S^T[kv, head] = K Q^T for the wave's 32 rows of the block (two tiles of 16 kv rows).
+    // The reads walk (step, tile) with a ring of KD reads in flight. Each tile's
+    // sum over the dims is split over QC accumulators (MFMA k-step c goes to
+    // chain c % QC) so that consecutive MFMAs do not wait on each other.
+    f32x4_t sacc[2];
     {
+      f32x4_t sch[2][QC];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int c = 0; c < QC; ++c) sch[nt][c] = f32x4_t{0, 0, 0, 0};
       constexpr int kSteps = FP8 ? 9 : 18;
       constexpr int kMainSteps = FP8 ? 8 : 16;  // steps whose slots lie in the main region
-      constexpr int kReads = kSteps * NT;
+      constexpr int kReads = kSteps * 2;
       u32x4_t kb[KD];
       auto kread = [&](int i) -> u32x4_t {
-        const int step = i / NT, nt = i % NT, o = nt & 1;
+        const int step = i / 2, nt = i % 2, o = nt & 1;
         if (step < kMainSteps)
           return lds_b128(mstage, k_main_base[o] + (uint32_t)(nt * 16 * L::kMainStride + step * 64));
         const int s2 = 4 * (step - kMainSteps) + g4;  // logical tail slot of this lane
@@ -502,85 +677,53 @@ void mla_decode_kernel(DecodeArgs a) {
       for (int i = 0; i < kReads; ++i) {
         if (i + KD - 1 < kReads) kb[(i + KD - 1) % KD] = kread(i + KD - 1);
         const u32x4_t raw = kb[i % KD];
-        const int step = i / NT, nt = i % NT;
+        const int step = i / 2, nt = i % 2;
         if constexpr (FP8) {
           // 16 fp8 = d in [64 step + 16 g4, +16): two k-steps of 8
-          sacc[nt] = mfma16(fp8x8_to_bf16x8(raw[0], raw[1]), qf[2 * step], sacc[nt]);
-          sacc[nt] = mfma16(fp8x8_to_bf16x8(raw[2], raw[3]), qf[2 * step + 1], sacc[nt]);
+          const int c0 = (2 * step) % QC, c1 = (2 * step + 1) % QC;
+          sch[nt][c0] = mfma16(fp8x8_to_bf16x8(raw[0], raw[1]), qf[2 * step], sch[nt][c0]);
+          sch[nt][c1] = mfma16(fp8x8_to_bf16x8(raw[2], raw[3]), qf[2 * step + 1], sch[nt][c1]);
         } else {
-          sacc[nt] = mfma16(__builtin_bit_cast(bf16x8_t, raw), qf[step], sacc[nt]);
+          sch[nt][step % QC] = mfma16(__builtin_bit_cast(bf16x8_t, raw), qf[step], sch[nt][step % QC]);
         }
         MLA_STEP_BARRIER();
       }
-    }
-
-    // ---- mask, online softmax (lane = one head row, 4*NT kv values per lane)
-    bf16x8_t pf[NU];
-    float alpha;
-    bool up;
-    {
-      const int lim0 = vis_end - kv0 - pg, lim1 = vis_end - kv0 - (pg ^ 1);
-      float mx = -__builtin_inff();
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+      for (int nt = 0; nt < 2; ++nt) {
+        sacc[nt] = sch[nt][0];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v = sacc[nt][r] * sscale;
-          v = nt * 16 + 2 * r < ((nt & 1) ? lim1 : lim0) ? v : -__builtin_inff();
-          sacc[nt][r] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = wave_max_16x4(mx);
-      const float old = m_ref;
-      up = mx > old + kRescaleSlack;
-      const float m_new = up ? mx : old;
-      alpha = up ? __builtin_amdgcn_exp2f(old - m_new) : 1.0f;  // old = -inf gives 0
-      m_ref = m_new;
-      const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;
-      float psum = 0.0f;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(sacc[nt][r] - m_use);
-          sacc[nt][r] = p;
-          psum += p;
-        }
-      l_part = l_part * alpha + psum;
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        u32x4_t w;
-        w[0] = pack_bf16x2(sacc[2 * u][0], sacc[2 * u][1]);
-        w[1] = pack_bf16x2(sacc[2 * u][2], sacc[2 * u][3]);
-        w[2] = pack_bf16x2(sacc[2 * u + 1][0], sacc[2 * u + 1][1]);
-        w[3] = pack_bf16x2(sacc[2 * u + 1][2], sacc[2 * u + 1][3]);
-        pf[u] = __builtin_bit_cast(bf16x8_t, w);
+        for (int c = 1; c < QC; ++c) sacc[nt] += sch[nt][c];
       }
     }
+
+    // ---- mask, online softmax
+    float alpha;
+    bool up;
+    const bf16x8_t pf =
+        softmax_block(sacc, sscale, vis_end - kv0 - pg, vis_end - kv0 - (pg ^ 1), m_ref, l_part, alpha, up);
     if (__builtin_amdgcn_ballot_w64(up)) {
 #pragma unroll
       for (int nt = 0; nt < 32; ++nt) o_acc[nt] *= alpha;
     }
 
     // ---- O^T[n, head] += V^T P^T ; V^T fragments by transposed LDS reads.
-    // P^T fragment u, lane (head, g4) holds kv rows 32u + pi_0(4g4 + r) (r < 4)
-    // then 32u + 16 + pi_1(4g4 + r); the V^T fragment holds the same rows, in
-    // the same order, for its latent column.
+    // Lane (head, g4) of P^T holds kv rows pi_0(4g4 + r) (r < 4) then
+    // 16 + pi_1(4g4 + r); the V^T fragment holds the same rows, in the same
+    // order, for its latent column.
     {
-      constexpr int kReads = 32 * NU;
+      constexpr int kReads = 32;
       u32x4_t vb[VD];
-      auto vread = [&](int j) -> u32x4_t {
-        const int u = j >> 5, nt = j & 31;
+      auto vread = [&](int nt) -> u32x4_t {
         u32x4_t w;
         if constexpr (FP8) {
-          const uint32_t off = v_base_lo + (uint32_t)(32 * u * L::kMainStride + nt * 16);
-          const i32x2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(i32x2_t))(mstage + off));
+          const i32x2_t raw =
+              __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(i32x2_t))(mstage + v_base_lo + (uint32_t)(nt * 16)));
           w[0] = (unsigned)raw[0];
           w[1] = (unsigned)raw[1];
           w[2] = 0;
           w[3] = 0;
         } else {
-          const uint32_t imm = (uint32_t)(32 * u * L::kMainStride + nt * 32);
+          const uint32_t imm = (uint32_t)(nt * 32);
           const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4_t))(mstage + v_base_lo + imm));
           const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4_t))(mstage + v_base_hi + imm));
           const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
@@ -599,12 +742,12 @@ void mla_decode_kernel(DecodeArgs a) {
         if (j + VD - 1 < kReads) vb[(j + VD - 1) % VD] = vread(j + VD - 1);
         const u32x4_t w = vb[j % VD];
         const bf16x8_t vf = FP8 ? fp8x8_to_bf16x8(w[0], w[1]) : __builtin_bit_cast(bf16x8_t, w);
-        o_acc[j & 31] = mfma16(vf, pf[j >> 5], o_acc[j & 31]);
+        o_acc[j] = mfma16(vf, pf, o_acc[j]);
         MLA_STEP_BARRIER();
       }
     }
   }
-  if (__builtin_amdgcn_ballot_w64(bad_page) && lane == 0) atomicOr(a.status, MLA_DEV_PAGE_OUT_OF_RANGE);
+  gather.report(a.status);
 
   // ---- epilogue. Each head tile has KW partial states (m_ref, l, o_acc) over
   // disjoint row sets, all relative to their own reference max. With KW > 1
@@ -619,8 +762,8 @@ void mla_decode_kernel(DecodeArgs a) {
     for (int nt = 0; nt < 32; ++nt) o_out[nt] = o_acc[nt];
   } else {
     __syncthreads();  // every wave is done with the ring
-    LDS_PTR(f32x4_t) ox = (LDS_PTR(f32x4_t))lds;                        // [NW][32][64]
-    LDS_PTR(float) mlx = (LDS_PTR(float))(lds + NW * 32 * 64 * 16);   // [NW][2][16]
+    LDS_PTR(f32x4_t) ox = (LDS_PTR(f32x4_t))lds;                       // [NW][32][64]
+    LDS_PTR(float) mlx = (LDS_PTR(float))(lds + NW * 32 * 64 * 16);  // [NW][2][16]
 #pragma unroll
     for (int nt = 0; nt < 32; ++nt) ox[(wave * 32 + nt) * 64 + lane] = o_acc[nt];
     if (g4 == 0) {
@@ -654,25 +797,18 @@ void mla_decode_kernel(DecodeArgs a) {
   const float inv = empty ? 0.0f : a.out_scale / l_tot;
   const float lse2 = empty ? -__builtin_inff() : m_fin + __log2f(l_tot);
   if (!row_ok) return;
-  const int nt0 = kw * kTilesOut;
-  if (n_b == 1) {
-    uint16_t* orow = a.out + (int64_t)row_out * kLatentDim;
+  const int rr = hw * 16 + i16;
+  const int64_t rec = (int64_t)a.partbase[b] + (int64_t)grp * n_b + chunk;
+  const int64_t prec_row = rec * a.rows_per_group + rr;
 #pragma unroll
-    for (int j = 0; j < kTilesOut; ++j) {
-      const f32x4_t o = o_out[j] * inv;
-      u32x2_t w;
-      w[0] = pack_bf16x2(o[0], o[1]);
-      w[1] = pack_bf16x2(o[2], o[3]);
-      *(u32x2_t*)(orow + (nt0 + j) * 16 + 4 * g4) = w;
+  for (int j = 0; j < kTilesOut; ++j)
+    store_out4(a, n_b == 1, row_out, prec_row, (kw * kTilesOut + j) * 16 + 4 * g4, o_out[j] * inv);
+  if (kw == 0 && g4 == 0) {
+    if (n_b == 1) {
+      if (a.lse) a.lse[row_out] = lse2 * kLn2;
+    } else {
+      a.part_lse[prec_row] = lse2;
     }
-    if (a.lse && kw == 0 && g4 == 0) a.lse[row_out] = lse2 * kLn2;
-  } else {
-    const int rr = hw * 16 + i16;
-    const int64_t rec = (int64_t)a.partbase[b] + (int64_t)grp * n_b + chunk;
-    float* prow = a.part_out + (rec * a.rows_per_group + rr) * kLatentDim;
-#pragma unroll
-    for (int j = 0; j < kTilesOut; ++j) *(f32x4_t*)(prow + (nt0 + j) * 16 + 4 * g4) = o_out[j] * inv;
-    if (kw == 0 && g4 == 0) a.part_lse[rec * a.rows_per_group + rr] = lse2;
   }
 }
 
@@ -770,10 +906,10 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
   }
 }
 
-template <bool FP8, int HW, int KW, int NS, int WPE, int KD, int VD>
+template <bool FP8, int HW, int KW, int NS, int WPE, int KD, int VD, int QC>
 int launch_decode_t(const DecodeArgs& a, int gx, int gy, int gz, hipStream_t st) {
-  hipLaunchKernelGGL((mla_decode_kernel<FP8, HW, KW, NS, WPE, KD, VD>), dim3(gx, gy, gz), dim3(HW * KW * 64), 0, st,
-                     a);
+  hipLaunchKernelGGL((mla_decode_kernel<FP8, HW, KW, NS, WPE, KD, VD, QC>), dim3(gx, gy, gz), dim3(HW * KW * 64), 0,
+                     st, a);
   return (int)hipGetLastError();
 }
 
@@ -790,18 +926,20 @@ int launch_plan(const PlanArgs& a, void* stream) {
 //   32 rows:  2 x 2 (64-row blocks)
 //   64 rows:  4 x 1 (32-row blocks)
 //   128 rows: 8 x 1 (32-row blocks, two waves per SIMD, 256 registers each)
+// Score sums are split over 4 accumulator chains (2 in the 128-row kernel,
+// where registers are short).
 int launch_decode(const DecodeArgs& a, int kv_dtype, int tile_class, int gx, int gy, int gz, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const bool fp8 = kv_dtype == MLA_KV_FP8_E4M3FN;
   switch (tile_class) {
-    case 0: return fp8 ? launch_decode_t<true, 1, 4, 2, 1, 8, 8>(a, gx, gy, gz, st)
-                       : launch_decode_t<false, 1, 2, 2, 1, 8, 8>(a, gx, gy, gz, st);
-    case 1: return fp8 ? launch_decode_t<true, 2, 2, 4, 1, 8, 8>(a, gx, gy, gz, st)
-                       : launch_decode_t<false, 2, 2, 2, 1, 8, 8>(a, gx, gy, gz, st);
-    case 2: return fp8 ? launch_decode_t<true, 4, 1, 8, 1, 8, 8>(a, gx, gy, gz, st)
-                       : launch_decode_t<false, 4, 1, 4, 1, 8, 8>(a, gx, gy, gz, st);
-    case 3: return fp8 ? launch_decode_t<true, 8, 1, 8, 2, 3, 3>(a, gx, gy, gz, st)
-                       : launch_decode_t<false, 8, 1, 4, 2, 3, 3>(a, gx, gy, gz, st);
+    case 0: return fp8 ? launch_decode_t<true, 1, 4, 2, 1, 8, 8, 4>(a, gx, gy, gz, st)
+                       : launch_decode_t<false, 1, 2, 2, 1, 8, 8, 4>(a, gx, gy, gz, st);
+    case 1: return fp8 ? launch_decode_t<true, 2, 2, 4, 1, 8, 8, 4>(a, gx, gy, gz, st)
+                       : launch_decode_t<false, 2, 2, 2, 1, 8, 8, 4>(a, gx, gy, gz, st);
+    case 2: return fp8 ? launch_decode_t<true, 4, 1, 8, 1, 8, 8, 4>(a, gx, gy, gz, st)
+                       : launch_decode_t<false, 4, 1, 4, 1, 8, 8, 4>(a, gx, gy, gz, st);
+    case 3: return fp8 ? launch_decode_t<true, 8, 1, 8, 2, 3, 3, 2>(a, gx, gy, gz, st)
+                       : launch_decode_t<false, 8, 1, 4, 2, 3, 3, 2>(a, gx, gy, gz, st);
   }
   return (int)hipErrorInvalidValue;
 }

@@ -64,7 +64,7 @@ const char* mla_status_string(mla_status_t s) {
 
 void mla_plan_options_default(mla_plan_options_t* out) {
   if (!out) return;
-  static const int32_t wg[4] = {1, 1, 2, 1};
+  static const int32_t wg[4] = {1, 1, 1, 1};
   static const int32_t cmin[4] = {256, 256, 256, 1024};
   static const int32_t cmax[4] = {8192, 8192, 4096, 4096};
   for (int c = 0; c < 4; ++c) {
@@ -117,7 +117,7 @@ mla_status_t mla_decode_plan_host(const mla_decode_params_t* params, const mla_p
     if (C > opt.chunk_max[cls]) C = opt.chunk_max[cls];
   }
   const int64_t max_chunks = cdiv(L, C);
-  if (G > 65535 || max_chunks > 0x7fffffff) return MLA_ERR_UNSUPPORTED;
+  if (G > 65535 || max_chunks > 0x7fffffff || B * max_chunks * G > 0x7fffffff) return MLA_ERR_UNSUPPORTED;
 
   mla_plan_t plan;
   std::memset(&plan, 0, sizeof(plan));
@@ -132,9 +132,10 @@ mla_status_t mla_decode_plan_host(const mla_decode_params_t* params, const mla_p
   plan.tile_class = cls;
   plan.chunk_len = int32_t(C);
   plan.max_chunks = int32_t(max_chunks);
-  plan.grid[0] = int32_t(max_chunks);
-  plan.grid[1] = int32_t(G);
-  plan.grid[2] = int32_t(B);
+  plan.work_capacity = B * max_chunks;
+  plan.grid[0] = int32_t(plan.work_capacity * G);
+  plan.grid[1] = 1;
+  plan.grid[2] = 1;
   plan.partial_capacity_records = B * G * max_chunks;
   uint64_t off = 0;
   plan.ws_status_offset = off;
@@ -147,6 +148,8 @@ mla_status_t mla_decode_plan_host(const mla_decode_params_t* params, const mla_p
   off = align256(off + uint64_t(plan.partial_capacity_records) * uint64_t(rows) * mla::kLatentDim * 4);
   plan.ws_part_lse_offset = off;
   off = align256(off + uint64_t(plan.partial_capacity_records) * uint64_t(rows) * 4);
+  plan.ws_work_offset = off;
+  off = align256(off + uint64_t(plan.work_capacity) * 8);
   plan.ws_bytes = off;
   *out_plan = plan;
   return MLA_OK;

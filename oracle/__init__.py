@@ -47,7 +47,7 @@ from .attention import (
     mla_decode_reference,
     mla_decode_reference_one,
 )
-from .planner import PlanOptions, reference_plan, device_plan_arrays
+from .planner import PlanOptions, reference_plan, device_plan_arrays, work_list
 
 __all__ = [
     "E4M3FN_VALUES",
@@ -65,4 +65,5 @@ __all__ = [
     "PlanOptions",
     "reference_plan",
     "device_plan_arrays",
+    "work_list",
 ]

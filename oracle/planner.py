@@ -25,7 +25,8 @@ The rule (all integer arithmetic):
     C    = force_chunk if set, else
            clamp(roundup(ceil(Lmax / want), 64), chunk_min[cls], chunk_max[cls])
            with want = max(1, floor(num_cu * wg_per_cu[cls] / (B * G)))
-    max_chunks = ceil(Lmax / C)        grid = (max_chunks, G, B)
+    max_chunks = ceil(Lmax / C)
+    work_capacity = B * max_chunks     decode grid = (work_capacity * G, 1, 1)
 
 Per sequence (device half): a sequence is valid when ``S <= ctx_b <= Lmax`` and
 its page list holds at least ``ceil(ctx_b / P)`` pages; then
@@ -33,6 +34,15 @@ its page list holds at least ``ceil(ctx_b / P)`` pages; then
 ``part_base_b`` is the exclusive prefix sum over ``b`` of
 ``(n_b if n_b > 1 else 0) * G``: partial records of sequence b, group g, chunk c
 sit at record ``part_base_b + g * n_b + c``.
+
+Work list (dispatch order; a design choice of this library, not from the
+pages): workgroups run longest work first so that the last workgroups on the
+CUs are short. Items are (sequence, chunk): every full chunk (exactly C rows)
+in (sequence, chunk) order; then each sequence's partial last chunk (length
+r = ctx - (n - 1) * C < C), by length class floor(16 * r / C) from the
+longest class down, ties by sequence; then one item (sequence, -1) per invalid
+sequence, whose rows are filled with NaN. Workgroup x of the decode grid runs
+item x // G for head group x % G.
 """
 
 from dataclasses import dataclass, field
@@ -45,6 +55,7 @@ TILE_CLASSES = (16, 32, 64, 128)
 STATUS_CTX_TOO_SHORT = 1  # context_lens[b] < seqlen_qo
 STATUS_CTX_TOO_LONG = 2  # context_lens[b] > max_context_len
 STATUS_TOO_FEW_PAGES = 4  # page list shorter than ceil(ctx / page_size)
+LENGTH_CLASSES = 16  # partial last chunks are dispatched by length class, longest first
 
 
 def _cdiv(a: int, b: int) -> int:
@@ -53,7 +64,7 @@ def _cdiv(a: int, b: int) -> int:
 
 @dataclass
 class PlanOptions:
-    wg_per_cu: List[int] = field(default_factory=lambda: [1, 1, 2, 1])
+    wg_per_cu: List[int] = field(default_factory=lambda: [1, 1, 1, 1])
     chunk_min: List[int] = field(default_factory=lambda: [256, 256, 256, 1024])
     chunk_max: List[int] = field(default_factory=lambda: [8192, 8192, 4096, 4096])
     force_chunk: int = 0
@@ -76,6 +87,7 @@ def reference_plan(batch, seqlen_qo, num_heads, max_context_len, num_cu, options
         C = min(max(C, o.chunk_min[cls]), o.chunk_max[cls])
     max_chunks = _cdiv(L, C)
     return {
+        "work_capacity": B * max_chunks,
         "heads_per_group": hpg,
         "num_groups": G,
         "rows_per_group": rows,
@@ -83,7 +95,7 @@ def reference_plan(batch, seqlen_qo, num_heads, max_context_len, num_cu, options
         "tile_class": cls,
         "chunk_len": C,
         "max_chunks": max_chunks,
-        "grid": (max_chunks, G, B),
+        "grid": (B * max_chunks * G, 1, 1),
         "partial_capacity_records": B * G * max_chunks,
     }
 
@@ -111,3 +123,21 @@ def device_plan_arrays(plan, seqlen_qo, max_context_len, page_size, context_lens
         part_base.append(running)
         running += (n if n > 1 else 0) * G
     return n_chunks, part_base, status
+
+
+def work_list(plan, n_chunks, context_lens):
+    """Work items (sequence, chunk) in dispatch order; chunk -1 marks an invalid sequence."""
+    C = plan["chunk_len"]
+    full, partial, invalid = [], [], []
+    for b, (n, ctx) in enumerate(zip(n_chunks, context_lens)):
+        n, ctx = int(n), int(ctx)
+        if n == 0:
+            invalid.append((b, -1))
+            continue
+        last = ctx - (n - 1) * C  # rows of the last chunk, 1..C
+        n_full = n if last == C else n - 1
+        full.extend((b, c) for c in range(n_full))
+        if last < C:
+            partial.append((LENGTH_CLASSES * last // C, b, n - 1))
+    partial.sort(key=lambda t: (-t[0], t[1]))
+    return full + [(b, c) for _, b, c in partial] + invalid

@@ -52,7 +52,8 @@ def test_struct_layouts_match_the_c_compiler(tmp_path):
 
 
 def test_abi_version_and_status_strings():
-    assert mla.abi_version() == 1
+    declared = int(re.search(r"#define MLA_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert mla.abi_version() == declared
     for code in range(6):
         assert mla.lib().mla_status_string(code)
     assert mla.lib().mla_status_string(99) == b"unknown status"
@@ -81,12 +82,13 @@ def test_host_plan_matches_reference_planner_bit_exactly(shape, force):
     assert plan.magic == 0x4D4C4131
     # workspace layout: 256-aligned, disjoint, in order, large enough for every partial
     offs = [plan.ws_status_offset, plan.ws_nchunks_offset, plan.ws_partbase_offset, plan.ws_part_out_offset,
-            plan.ws_part_lse_offset, plan.ws_bytes]
+            plan.ws_part_lse_offset, plan.ws_work_offset, plan.ws_bytes]
     assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
     assert plan.ws_nchunks_offset - plan.ws_status_offset >= 16
     assert plan.ws_partbase_offset - plan.ws_nchunks_offset >= 4 * B
     assert plan.ws_part_lse_offset - plan.ws_part_out_offset >= 4 * 512 * ref["rows_per_group"] * ref["partial_capacity_records"]
-    assert plan.ws_bytes - plan.ws_part_lse_offset >= 4 * ref["rows_per_group"] * ref["partial_capacity_records"]
+    assert plan.ws_work_offset - plan.ws_part_lse_offset >= 4 * ref["rows_per_group"] * ref["partial_capacity_records"]
+    assert plan.ws_bytes - plan.ws_work_offset >= 8 * ref["work_capacity"]
     assert mla.workspace_size(p, mla.make_options(force_chunk=force), 256) == plan.ws_bytes
 
 

@@ -77,6 +77,7 @@ def check_plan_arrays(case, dec):
     rn, rbase, rstatus = oracle.device_plan_arrays(ref, case.seqlen_qo, case.max_context_len, case.page_size,
                                                    case.context_lens, case.kv_indptr)
     assert n == rn and base == rbase and status == rstatus
+    assert mla.read_work_list(dec.plan, dec.workspace) == oracle.work_list(ref, rn, case.context_lens)
     return status
 
 
@@ -112,7 +113,8 @@ def test_tiny_workload_forced_split_exercises_the_combine():
 GRID = []
 for kv_dtype in ("bf16", "fp8_e4m3fn"):
     for (S, H, causal) in ((1, 12, False), (1, 16, False), (4, 16, True), (2, 32, False), (1, 128, False),
-                           (4, 32, True), (3, 5, True), (1, 40, False), (2, 16, True), (1, 20, False)):
+                           (4, 32, True), (3, 5, True), (1, 40, False), (2, 16, True), (1, 20, False),
+                           (2, 128, False), (3, 64, True)):
         for P in (1, 16, 64):
             GRID.append((kv_dtype, S, H, causal, P))
 
@@ -145,6 +147,7 @@ def test_invalid_sequences_get_nan_rows_and_status_bits():
     case = make_case(batch=4, seqlen_qo=2, num_heads=16, ctx=[40, 1, 90, 33], page_size=16, kv_dtype="bf16",
                      seed=78, max_context_len=80)
     dec, out, lse = run(case, options(force_chunk=64))
+    check_plan_arrays(case, dec)
     n, _, status = mla.read_plan_arrays(dec.plan, dec.workspace)
     assert status == (mla.DEV_CTX_TOO_SHORT | mla.DEV_CTX_TOO_LONG)
     assert n[1] == 0 and n[2] == 0

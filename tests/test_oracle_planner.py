@@ -3,7 +3,7 @@
 import numpy as np
 import pytest
 
-from oracle import PlanOptions, reference_plan, device_plan_arrays
+from oracle import PlanOptions, reference_plan, device_plan_arrays, work_list
 from oracle.planner import STATUS_CTX_TOO_SHORT, STATUS_CTX_TOO_LONG, STATUS_TOO_FEW_PAGES
 
 
@@ -29,15 +29,17 @@ def test_plan_structure(shape):
     assert TR in (16, 32, 64, 128) and TR >= rows and (TR == 16 or TR // 2 < rows)
     assert C % 64 == 0 and C >= 64
     assert p["max_chunks"] * C >= L and (p["max_chunks"] - 1) * C < L
-    assert p["grid"] == (p["max_chunks"], G, B)
+    assert p["work_capacity"] == B * p["max_chunks"]
+    assert p["grid"] == (p["work_capacity"] * G, 1, 1)
 
 
 def test_plan_values_for_the_benchmark_shapes():
     # Hand-derived from the rule with the default options and 256 CUs.
     p = reference_plan(64, 1, 128, 8192, 256)
     assert (p["heads_per_group"], p["num_groups"], p["tile_rows"], p["chunk_len"], p["max_chunks"]) == (128, 1, 128, 2048, 4)
+    # 16 heads x 4 tokens: want = floor(256 / 128) = 2 -> ceil(5200 / 2) = 2600 -> 2624 rows, 2 chunks
     p = reference_plan(128, 4, 16, 5200, 256)
-    assert (p["heads_per_group"], p["tile_rows"], p["chunk_len"], p["max_chunks"]) == (16, 64, 1344, 4)
+    assert (p["heads_per_group"], p["tile_rows"], p["chunk_len"], p["max_chunks"]) == (16, 64, 2624, 2)
     p = reference_plan(256, 1, 128, 23333, 256)
     assert (p["chunk_len"], p["max_chunks"]) == (4096, 6)
     # 12 heads, one sequence: want = 256 -> ceil(109440 / 256) = 428 -> 448 rows, 245 chunks
@@ -84,3 +86,39 @@ def test_device_status_bits():
     n, base, status = device_plan_arrays(p, 2, 100, 1, lens, indptr)
     assert status == STATUS_CTX_TOO_SHORT | STATUS_CTX_TOO_LONG | STATUS_TOO_FEW_PAGES
     assert n[:3] == [0, 0, 0] and n[3] == _cdiv(50, p["chunk_len"])
+
+
+def test_work_list_hand_example():
+    # C = 64: ctx 200 -> chunks of 64, 64, 64, 8 (last: class 16*8//64 = 2);
+    # ctx 64 -> one full chunk; ctx 100 -> 64 + 36 (class 9); ctx 0 < S -> invalid;
+    # ctx 120 -> 64 + 56 (class 14)
+    plan = reference_plan(5, 1, 16, 200, 256, PlanOptions(force_chunk=64))
+    lens = [200, 64, 100, 0, 120]
+    n, _, status = device_plan_arrays(plan, 1, 200, 1, lens, [0, 200, 264, 364, 364, 484])
+    assert n == [4, 1, 2, 0, 2] and status == 1
+    assert work_list(plan, n, lens) == [(0, 0), (0, 1), (0, 2), (1, 0), (2, 0), (4, 0),
+                                        (4, 1), (2, 1), (0, 3), (3, -1)]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_work_list_covers_every_chunk_once_longest_first(seed):
+    rng = np.random.default_rng(100 + seed)
+    B, S = int(rng.integers(1, 300)), int(rng.integers(1, 5))
+    L = int(rng.integers(S, 6000))
+    lens = rng.integers(0, L + 1, size=B)
+    plan = reference_plan(B, S, 16, L, 256, PlanOptions(force_chunk=int(rng.choice([0, 64, 256, 1024]))))
+    C = plan["chunk_len"]
+    indptr = np.concatenate([[0], np.cumsum(lens)])  # page size 1: one page per row
+    n, _, _ = device_plan_arrays(plan, S, L, 1, lens, indptr)
+    items = work_list(plan, n, lens)
+    assert len(items) <= plan["work_capacity"]
+    want = {(b, c) for b in range(B) for c in range(n[b])} | {(b, -1) for b in range(B) if n[b] == 0}
+    assert len(items) == len(want) and set(items) == want
+    # dispatch order: class (full chunk 16, partial floor(16 r / C), invalid -1) never rises,
+    # and within a class the items follow (sequence, chunk) order
+    keys = []
+    for b, c in items:
+        r = -1 if c < 0 else min(C, int(lens[b]) - c * C)
+        keys.append((-1 if r < 0 else 16 * r // C, b, c))
+    assert all(keys[i][0] >= keys[i + 1][0] for i in range(len(keys) - 1))
+    assert all(keys[i][1:] < keys[i + 1][1:] for i in range(len(keys) - 1) if keys[i][0] == keys[i + 1][0])
