@@ -1,6 +1,7 @@
 """Benchmark: MLA decode over a paged latent cache on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --copy-probe     (a plain 1 GiB device copy, to scale the HBM byte counters)
 
 One step = one call of the hot path (mla_decode + mla_split_combine) over the
 whole batch, inputs resident in HBM. Between steps a 1 GiB buffer is read
@@ -13,7 +14,10 @@ Roofline accounting (per decode launch):
   algorithmic bytes = sum_b ctx_b * 576 * e (each cache row read once; e = 2 bf16, 1 fp8)
                       + B*S*H*576*2 (q) + B*S*H*512*2 (out) + 4*(B+1) + 4*pages + 4*B (page table, lengths)
   algorithmic flops = 2 * H * (visible row visits) * (576 + 512)
-against 8 TB/s HBM and 2.5 PFLOP/s dense bf16 MFMA.
+against 8 TB/s HBM and 2.5 PFLOP/s dense bf16 MFMA. roofline.traffic is the HBM
+rate implied by the rocprofv3 FETCH_SIZE + WRITE_SIZE counters of the decode
+kernel recorded under profiles/ for this workload, taken only while the kernel
+sources still hash to the value recorded with them (else null).
 """
 
 import argparse
@@ -24,6 +28,8 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+CSRC = os.path.join(ROOT, "mla_paged_latent_02_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -46,45 +52,83 @@ def algorithmic_counts(case):
     return nbytes, flops
 
 
-def cpu_baseline(case, budget_s=20.0):
-    """The oracle as it stands, timed on a bounded sample of sequences."""
+def kernel_source_digest():
+    """First 16 hex digits of the sha256 over the library's C/HIP sources and its header."""
+    import hashlib
+    h = hashlib.sha256()
+    paths = [os.path.join(CSRC, n) for n in sorted(os.listdir(CSRC)) if n.endswith((".hip", ".cpp", ".h"))]
+    for path in paths + [os.path.join(ROOT, "include", "mla_decode.h")]:
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload):
+    """HBM bytes per decode launch from the committed counter summary, if it matches these sources."""
+    import re
+    path = os.path.join(PROFILES, f"mla_decode_kernel_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        fields = dict(re.findall(r"^- (\w+): (\S+)\s*$", f.read(), flags=re.M))
+    if fields.get("kernel_source_sha256_16") != kernel_source_digest():
+        return None
+    return float(fields["hbm_bytes_per_launch"])
+
+
+def copy_probe(nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of known size: FETCH_SIZE / WRITE_SIZE of this kernel scale the counters."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def cpu_baseline(case, min_s=10.0, max_s=30.0):
+    """The oracle as it stands, timed on a bounded sample: sequences of the batch in order, cycling
+    through the batch again until at least min_s of oracle work (or max_s) has run; scaled by cache rows."""
     import numpy as np
     import oracle
     cores = len(os.sched_getaffinity(0))
-    t_seq = []
-    order = list(range(case.batch))
-    t0 = time.perf_counter()
-    for b in order:
+    secs, rows_done, evals = 0.0, 0, 0
+    while secs < min_s and (secs < max_s or evals == 0):
+        b = evals % case.batch
         s0 = time.perf_counter()
         oracle.mla_decode_reference_one(case.q_bits, case.cache_raw, case.kv_dtype, case.kv_scale, case.kv_indptr,
                                         case.kv_page_indices, case.context_lens, case.page_size,
                                         case.softmax_scale, case.causal, b)
-        t_seq.append((b, time.perf_counter() - s0))
-        if time.perf_counter() - t0 > budget_s:
-            break
-    done = [b for b, _ in t_seq]
-    secs = sum(t for _, t in t_seq)
-    rows_done = int(case.context_lens[done].astype(np.int64).sum())
+        secs += time.perf_counter() - s0
+        rows_done += int(case.context_lens[b])
+        evals += 1
     rows_all = int(case.context_lens.astype(np.int64).sum())
     per_call_us = secs * rows_all / rows_done * 1e6
     return {"value": per_call_us, "unit": "us", "cores": cores, "kind": "oracle",
-            "sample": f"{len(done)} of {case.batch} sequences ({rows_done} cache rows, {secs:.1f} s), "
-                      f"scaled by cache rows to the full batch; float64 numpy, BLAS threads = {cores}"}
+            "sample": f"{evals} sequence evaluations over a batch of {case.batch} ({rows_done} cache rows, "
+                      f"{secs:.1f} s), scaled by cache rows to one full call; float64 numpy, BLAS threads = {cores}"}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this decode path has no multi-GPU mode (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe()
+        return
 
     if not args.no_cpu_baseline:
         n = str(len(os.sched_getaffinity(0)))
@@ -160,7 +204,10 @@ def main():
         tf = flops / dec_s / 1e12
         roof = {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": tf / MFMA_BF16_PEAK_TFLOPS}
-    roof["traffic"] = None
+    traffic_bytes = recorded_traffic(args.workload)
+    roof["traffic"] = None if traffic_bytes is None else traffic_bytes / dec_s / 1e9
+    roof["traffic_bytes_per_launch"] = traffic_bytes
+    roof["kernel_source_sha256_16"] = kernel_source_digest()
     roof["kernel"] = "mla_decode_kernel"
     roof["kernel_avg_us"] = float(np.mean(dec_ms) * 1e3)
     roof["alg_bytes"] = nbytes
