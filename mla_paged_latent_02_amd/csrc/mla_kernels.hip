@@ -261,6 +261,11 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory");
 }
 
+// The same for 4 bytes per lane (global_load_lds_dword): lane i lands at lds_addr + 4*lane.
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds_addr) : "memory");
+}
+
 // s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -268,17 +273,17 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Wait until at most min(k, MAXK) * K DMA instructions of this wave are pending.
-template <int K, int MAXK>
+// Wait until at most C + min(k, MAXK) * K vector-memory instructions of this wave are pending.
+template <int K, int MAXK, int C>
 __device__ __forceinline__ void wait_vmcnt_blocks(int k) {
   if constexpr (MAXK >= 1) {
     if (k >= MAXK) {
-      wait_vmcnt<MAXK * K>();
+      wait_vmcnt<C + MAXK * K>();
       return;
     }
-    wait_vmcnt_blocks<K, MAXK - 1>(k);
+    wait_vmcnt_blocks<K, MAXK - 1, C>(k);
   } else {
-    wait_vmcnt<0>();
+    wait_vmcnt<C>();
   }
 }
 
@@ -293,13 +298,19 @@ __device__ __forceinline__ int perm_row(int m, int odd) {
 // min(c_start + blk*BN + w*RPW + r, c_end - 1): rows past the chunk repeat its
 // last row, whose scores are masked. Protocol, per block blk of the loop:
 //   wait(blk); __syncthreads(); advance(blk); ... read stage blk % NS ...
-// The page ids come either
-//  - (ring of more than two stages) from scalar loads, so that the only
-//    vector-memory instructions in the loop are the kDmaInsts DMA
-//    instructions per block and the ring can wait for its oldest block alone;
-//  - (two stages) from one vector load per block (lane r: row r), issued
-//    right after the previous block's DMA: the loop waits for all its loads
-//    at the top anyway, and no scalar register has to hold a block of ids.
+// Page ids never come through scalar loads inside the loop: an outstanding
+// scalar load makes the first LDS wait of the block drain everything (the
+// counter is shared and scalar loads return out of order).
+//  - Ring of more than two stages: the page ids of block j (lane r: row r)
+//    are copied by DMA (global_load_lds_dword) into a small LDS ring of NS
+//    entries at iteration j - 2NS + 2, ahead of block j - NS + 1's gather in
+//    issue order. Loads complete in order, so the wait for block k's gather
+//    also covers the ids that iteration k needs; every iteration issues one
+//    id copy (block index clamped) and kDmaInsts gather instructions per
+//    valid block, and the wait counts both.
+//  - Two stages: one vector load per block into a register (lane r: row r),
+//    issued right after the previous block's gather: the loop waits for all
+//    its loads at the top anyway.
 // A page id outside the pool is replaced by page 0 and noted in bad_page.
 template <bool FP8, int NW, int BN, int NS>
 struct BlockGather {
@@ -307,29 +318,30 @@ struct BlockGather {
   static constexpr int RPW = BN / NW;  // rows each wave gathers per block
   static constexpr int kTailRowsPerInst = 64 / L::kTailSlots;
   static constexpr int kTailInsts = (RPW + kTailRowsPerInst - 1) / kTailRowsPerInst;
-  static constexpr int kDmaInsts = RPW + kTailInsts;  // vector-memory instructions per wave per block
+  static constexpr int kDmaInsts = RPW + kTailInsts;  // gather instructions per wave per block
   static constexpr bool kVecPages = NS == 2;
+  static constexpr int kPidRingBytes = kVecPages ? 0 : NS * BN * 4;
   static_assert(RPW >= 1 && BN % NW == 0, "row split");
-  static_assert((NS - 2) * kDmaInsts <= 63, "vmcnt range");
+  static_assert(kVecPages || RPW % 4 == 0, "page ids are read four at a time");
+  static_assert((NS - 2) * (kDmaInsts + 1) <= 63, "vmcnt range");
 
   const uint8_t* cache;
   const int32_t* page_ids;
-  const __attribute__((address_space(4))) int32_t* page_ids_s;
   int64_t num_pages;
-  uint32_t magic, lds_base;
+  uint32_t magic, lds_base, pid_base;
   int c_start, c_end, nblk, page_base, P, wave, lane, tslot, trow, my_row;
   bool bad_page;
-  int v_page;                       // two stages: lane r < RPW holds the page id of row r of the next block
-  int page_n[kVecPages ? 1 : RPW];  // more stages: page ids of the next block
+  int v_page;  // two stages: lane r < RPW holds the page id of row r of the next block
 
-  __device__ __forceinline__ BlockGather(const DecodeArgs& a, uint32_t lds_base_, int c_start_, int c_end_,
-                                         int page_base_, int wave_, int lane_)
+  // pid_lds: LDS address of kPidRingBytes for the page-id ring (unused with two stages)
+  __device__ __forceinline__ BlockGather(const DecodeArgs& a, uint32_t lds_base_, uint32_t pid_lds, int c_start_,
+                                         int c_end_, int page_base_, int wave_, int lane_)
       : cache(a.cache),
         page_ids(a.kv_page_indices),
-        page_ids_s((const __attribute__((address_space(4))) int32_t*)a.kv_page_indices),
         num_pages(a.num_pages),
         magic(a.page_div_magic),
         lds_base(lds_base_),
+        pid_base(pid_lds),
         c_start(c_start_),
         c_end(c_end_),
         nblk((c_end_ - c_start_ + BN - 1) / BN),
@@ -381,19 +393,21 @@ struct BlockGather {
         lds_base + stage_off + (uint32_t)(L::kTailBase + (wave * RPW + m * kTailRowsPerInst) * L::kTailBytes));
     if (m * kTailRowsPerInst + trow < RPW) dma16(src, dst);
   }
-  __device__ __forceinline__ void fetch(int blk) {
-    if constexpr (kVecPages) {
-      int q, rem;
-      page_pos(row_kv(blk, my_row), q, rem);
-      v_page = page_ids[page_base + q];
-    } else {
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        int q, rem;
-        page_pos(__builtin_amdgcn_readfirstlane(row_kv(blk, r)), q, rem);
-        page_n[r] = page_ids_s[page_base + q];
-      }
-    }
+  // LDS address of this wave's page ids of block j in the ring
+  __device__ __forceinline__ uint32_t pid_slot(int j) const {
+    return pid_base + (uint32_t)(((j % NS) * BN + wave * RPW) * 4);
+  }
+  // ring stages: copy the page ids of block j (clamped to the chunk) into the ring
+  __device__ __forceinline__ void pid_copy(int j) const {
+    int q, rem;
+    page_pos(row_kv(min(j, nblk - 1), my_row), q, rem);
+    if (lane < RPW) dma4(page_ids + page_base + q, __builtin_amdgcn_readfirstlane(pid_slot(j)));
+  }
+  // two stages: load the page ids of block blk into v_page
+  __device__ __forceinline__ void fetch_v(int blk) {
+    int q, rem;
+    page_pos(row_kv(blk, my_row), q, rem);
+    v_page = page_ids[page_base + q];
   }
   __device__ __forceinline__ void issue(int blk) {
     if constexpr (kVecPages) {
@@ -406,12 +420,21 @@ struct BlockGather {
       for (int m = 0; m < kTailInsts; ++m)
         issue_tail(blk, m, __builtin_amdgcn_ds_bpermute((m * kTailRowsPerInst + trow) << 2, slot_v));
     } else {
+      // the wave's RPW page ids, four per (uniform-address) LDS read
+      int pid[RPW];
+      LDS_PTR(uint8_t) ring = (LDS_PTR(uint8_t))(uintptr_t)0;
+#pragma unroll
+      for (int r4 = 0; r4 < RPW; r4 += 4) {
+        const u32x4_t v = *(LDS_PTR(u32x4_t))(ring + pid_slot(blk) + 4 * r4);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) pid[r4 + k] = __builtin_amdgcn_readfirstlane((int)v[k]);
+      }
       int slot[RPW];
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
         int q, rem;
         page_pos(__builtin_amdgcn_readfirstlane(row_kv(blk, r)), q, rem);
-        slot[r] = checked(page_n[r]) * P + rem;
+        slot[r] = checked(pid[r]) * P + rem;
         issue_main_row(blk, r, slot[r]);
       }
 #pragma unroll
@@ -424,27 +447,44 @@ struct BlockGather {
       }
     }
   }
-  // prologue: blocks 0 .. NS-2 in flight, page ids of block NS-1 fetched
+  // prologue: blocks 0 .. NS-2 in flight
   __device__ __forceinline__ void start() {
+    if constexpr (kVecPages) {
+      fetch_v(0);
+      issue(0);
+      if (1 < nblk) fetch_v(1);
+    } else {
+      // ids of blocks 0 .. NS-2, then iterations -(NS-1) .. -1 in loop order (id copy of block
+      // i + 2NS - 2, gather of block i + NS - 1), so that the loop's wait counts hold from block 0
 #pragma unroll
-    for (int i = 0; i < NS - 1; ++i) {
-      if (i < nblk) {
-        fetch(i);
-        issue(i);
+      for (int j = 0; j < NS - 1; ++j) pid_copy(j);
+      wait_vmcnt<0>();
+#pragma unroll
+      for (int i = -(NS - 1); i < 0; ++i) {
+        pid_copy(i + 2 * NS - 2);
+        if (i + NS - 1 < nblk) issue(i + NS - 1);
       }
     }
-    if (NS - 1 < nblk) fetch(NS - 1);
   }
   // this wave's loads of block blk have landed (the caller then synchronises the workgroup)
   __device__ __forceinline__ void wait(int blk) const {
-    // blocks issued after blk so far: blk+1 .. min(blk+NS-2, nblk-1)
-    wait_vmcnt_blocks<kDmaInsts, NS - 2>(nblk - 1 - blk);
+    if constexpr (kVecPages) {
+      wait_vmcnt<0>();
+    } else {
+      // after block blk's gather: NS-2 id copies and the gathers of blocks blk+1 .. min(blk+NS-2, nblk-1)
+      wait_vmcnt_blocks<kDmaInsts, NS - 2, NS - 2>(nblk - 1 - blk);
+    }
   }
   // after the barrier that publishes block blk: the stage of block blk-1 is free
   __device__ __forceinline__ void advance(int blk) {
-    if (blk + NS - 1 < nblk) {
-      issue(blk + NS - 1);
-      if (blk + NS < nblk) fetch(blk + NS);
+    if constexpr (kVecPages) {
+      if (blk + 1 < nblk) {
+        issue(blk + 1);
+        if (blk + 2 < nblk) fetch_v(blk + 2);
+      }
+    } else {
+      pid_copy(blk + 2 * NS - 2);
+      if (blk + NS - 1 < nblk) issue(blk + NS - 1);
     }
   }
   __device__ __forceinline__ void report(uint32_t* status) const {
@@ -539,16 +579,21 @@ __device__ __forceinline__ void store_out4(const DecodeArgs& a, bool final_row, 
 // fragments and its 16 x 512 fp32 output stay in registers for the whole
 // chunk) and cache rows [32 kw, 32 kw + 32) of every block of BN = 32 KW rows,
 // with its own online-softmax state. The KW states of a head tile are merged
-// through LDS at the end of the chunk.
+// through LDS at the end of the chunk by wave (hw, 0).
 template <bool FP8, int HW, int KW, int NS>
 struct DecodeCfg {
   static constexpr int kWaves = HW * KW;
   static constexpr int kBlockN = 32 * KW;  // cache rows per block
   using Gather = BlockGather<FP8, kWaves, kBlockN, NS>;
   using L = typename Gather::L;
-  static constexpr int kRingBytes = NS * L::kBlockBytes;
-  // merge area after the loop: every wave's 16 x 512 fp32 output, then its max and sum per head
-  static constexpr int kMergeBytes = KW > 1 ? kWaves * (32 * 64 * 16 + 2 * 16 * 4) : 0;
+  static constexpr int kRingBytes = NS * L::kBlockBytes + Gather::kPidRingBytes;  // stages, then page ids
+  // Merge area after the loop: 16 x 512 fp32 outputs, then a max and a sum per head, of every
+  // wave when they all fit (each wave then merges a column slice), else of the waves with kw > 0
+  // (wave (hw, 0) then merges the whole tile).
+  static constexpr int kStateBytes = 32 * 64 * 16 + 2 * 16 * 4;
+  static constexpr bool kMergeSpread = KW > 1 && kWaves * kStateBytes <= kRingBytes;
+  static constexpr int kMergeWaves = KW == 1 ? 0 : kMergeSpread ? kWaves : (KW - 1) * HW;
+  static constexpr int kMergeBytes = kMergeWaves * kStateBytes;
   static constexpr int kLdsBytes = kRingBytes > kMergeBytes ? kRingBytes : kMergeBytes;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
@@ -610,7 +655,8 @@ void mla_decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int nt = 0; nt < 32; ++nt) o_acc[nt] = f32x4_t{0, 0, 0, 0};
 
-  typename Cfg::Gather gather(a, (uint32_t)(uintptr_t)lds, c_start, c_end, a.kv_indptr[b], wave, lane);
+  typename Cfg::Gather gather(a, (uint32_t)(uintptr_t)lds, (uint32_t)(uintptr_t)lds + NS * L::kBlockBytes, c_start,
+                              c_end, a.kv_indptr[b], wave, lane);
   const int nblk = gather.nblk;
 
   // Per-lane LDS offsets that do not change over the loop; each access adds a
@@ -750,47 +796,60 @@ void mla_decode_kernel(DecodeArgs a) {
   gather.report(a.status);
 
   // ---- epilogue. Each head tile has KW partial states (m_ref, l, o_acc) over
-  // disjoint row sets, all relative to their own reference max. With KW > 1
-  // they go through LDS and wave (hw, kw) merges latent columns
-  // [512 kw / KW, 512 (kw + 1) / KW) of head tile hw.
-  constexpr int kTilesOut = 32 / KW;  // 16-column output tiles per wave
+  // disjoint row sets, each relative to its own reference max; with KW > 1
+  // they are merged through LDS (see DecodeCfg: by column slices over all
+  // waves, or by wave (hw, 0) alone). Wave (hw, kw) then stores 16-column
+  // output tiles [nt0, nt0 + ntiles) of head tile hw.
   float l_tot = wave_sum_16x4(l_part);
   float m_fin = m_ref;
-  f32x4_t o_out[kTilesOut];
-  if constexpr (KW == 1) {
-#pragma unroll
-    for (int nt = 0; nt < 32; ++nt) o_out[nt] = o_acc[nt];
-  } else {
+  int nt0 = 0, ntiles = 32;
+  if constexpr (KW > 1) {
     __syncthreads();  // every wave is done with the ring
-    LDS_PTR(f32x4_t) ox = (LDS_PTR(f32x4_t))lds;                       // [NW][32][64]
-    LDS_PTR(float) mlx = (LDS_PTR(float))(lds + NW * 32 * 64 * 16);  // [NW][2][16]
+    LDS_PTR(f32x4_t) ox = (LDS_PTR(f32x4_t))lds;                                     // [slot][32][64]
+    LDS_PTR(float) mlx = (LDS_PTR(float))(lds + Cfg::kMergeWaves * 32 * 64 * 16);  // [slot][2][16]
+    // LDS slot of wave (hw, k)'s state
+    auto slot_of = [&](int k) { return Cfg::kMergeSpread ? k * HW + hw : (k - 1) * HW + hw; };
+    if (Cfg::kMergeSpread || kw > 0) {
+      const int slot = slot_of(kw);
 #pragma unroll
-    for (int nt = 0; nt < 32; ++nt) ox[(wave * 32 + nt) * 64 + lane] = o_acc[nt];
-    if (g4 == 0) {
-      mlx[wave * 32 + i16] = m_ref;
-      mlx[wave * 32 + 16 + i16] = l_tot;
+      for (int nt = 0; nt < 32; ++nt) ox[(slot * 32 + nt) * 64 + lane] = o_acc[nt];
+      if (g4 == 0) {
+        mlx[slot * 32 + i16] = m_ref;
+        mlx[slot * 32 + 16 + i16] = l_tot;
+      }
     }
     __syncthreads();
-    float ms[KW], wt[KW];
-    m_fin = -__builtin_inff();
+    if (!Cfg::kMergeSpread && kw > 0) return;
+    float ms[KW], ls[KW], wt[KW];
 #pragma unroll
     for (int k = 0; k < KW; ++k) {
-      ms[k] = mlx[(hw + HW * k) * 32 + i16];
-      m_fin = fmaxf(m_fin, ms[k]);
+      const bool own = !Cfg::kMergeSpread && k == 0;
+      ms[k] = own ? m_ref : mlx[slot_of(k) * 32 + i16];
+      ls[k] = own ? l_tot : mlx[slot_of(k) * 32 + 16 + i16];
     }
+    m_fin = ms[0];
+#pragma unroll
+    for (int k = 1; k < KW; ++k) m_fin = fmaxf(m_fin, ms[k]);
     l_tot = 0.0f;
 #pragma unroll
     for (int k = 0; k < KW; ++k) {
       wt[k] = ms[k] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(ms[k] - m_fin);
-      l_tot += wt[k] * mlx[(hw + HW * k) * 32 + 16 + i16];
+      l_tot += wt[k] * ls[k];
+    }
+    if (Cfg::kMergeSpread) {
+      nt0 = kw * (32 / KW);
+      ntiles = 32 / KW;
     }
 #pragma unroll
-    for (int j = 0; j < kTilesOut; ++j) {
-      const int nt = kw * kTilesOut + j;
+    for (int nt = 0; nt < 32; ++nt) {
+      if (Cfg::kMergeSpread && (nt < nt0 || nt >= nt0 + ntiles)) continue;
       f32x4_t acc = f32x4_t{0, 0, 0, 0};
 #pragma unroll
-      for (int k = 0; k < KW; ++k) acc += wt[k] * ox[((hw + HW * k) * 32 + nt) * 64 + lane];
-      o_out[j] = acc;
+      for (int k = 0; k < KW; ++k) {
+        const bool own = !Cfg::kMergeSpread && k == 0;
+        acc += wt[k] * (own ? o_acc[nt] : ox[(slot_of(k) * 32 + nt) * 64 + lane]);
+      }
+      o_acc[nt] = acc;
     }
   }
   const bool empty = !(l_tot > 0.0f);
@@ -801,8 +860,8 @@ void mla_decode_kernel(DecodeArgs a) {
   const int64_t rec = (int64_t)a.partbase[b] + (int64_t)grp * n_b + chunk;
   const int64_t prec_row = rec * a.rows_per_group + rr;
 #pragma unroll
-  for (int j = 0; j < kTilesOut; ++j)
-    store_out4(a, n_b == 1, row_out, prec_row, (kw * kTilesOut + j) * 16 + 4 * g4, o_out[j] * inv);
+  for (int nt = 0; nt < 32; ++nt)
+    if (nt >= nt0 && nt < nt0 + ntiles) store_out4(a, n_b == 1, row_out, prec_row, nt * 16 + 4 * g4, o_acc[nt] * inv);
   if (kw == 0 && g4 == 0) {
     if (n_b == 1) {
       if (a.lse) a.lse[row_out] = lse2 * kLn2;
@@ -924,7 +983,7 @@ int launch_plan(const PlanArgs& a, void* stream) {
 // noted; stages = as many blocks as the LDS holds):
 //   16 rows:  1 x 4 (fp8, 128-row blocks) or 1 x 2 (bf16, 64-row blocks)
 //   32 rows:  2 x 2 (64-row blocks)
-//   64 rows:  4 x 1 (32-row blocks)
+//   64 rows:  4 x 2 (64-row blocks, two waves per SIMD, 256 registers each)
 //   128 rows: 8 x 1 (32-row blocks, two waves per SIMD, 256 registers each)
 // Score sums are split over 4 accumulator chains (2 in the 128-row kernel,
 // where registers are short).
@@ -936,8 +995,8 @@ int launch_decode(const DecodeArgs& a, int kv_dtype, int tile_class, int gx, int
                        : launch_decode_t<false, 1, 2, 2, 1, 8, 8, 4>(a, gx, gy, gz, st);
     case 1: return fp8 ? launch_decode_t<true, 2, 2, 4, 1, 8, 8, 4>(a, gx, gy, gz, st)
                        : launch_decode_t<false, 2, 2, 2, 1, 8, 8, 4>(a, gx, gy, gz, st);
-    case 2: return fp8 ? launch_decode_t<true, 4, 1, 8, 1, 8, 8, 4>(a, gx, gy, gz, st)
-                       : launch_decode_t<false, 4, 1, 4, 1, 8, 8, 4>(a, gx, gy, gz, st);
+    case 2: return fp8 ? launch_decode_t<true, 4, 2, 4, 2, 3, 3, 2>(a, gx, gy, gz, st)
+                       : launch_decode_t<false, 4, 2, 2, 2, 3, 3, 2>(a, gx, gy, gz, st);
     case 3: return fp8 ? launch_decode_t<true, 8, 1, 8, 2, 3, 3, 2>(a, gx, gy, gz, st)
                        : launch_decode_t<false, 8, 1, 4, 2, 3, 3, 2>(a, gx, gy, gz, st);
   }
