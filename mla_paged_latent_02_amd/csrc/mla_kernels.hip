@@ -976,8 +976,9 @@ int launch_plan(const PlanArgs& a, void* stream) {
 //   32 rows:  2 x 2 (64-row blocks)
 //   64 rows:  4 x 2 (64-row blocks, two waves per SIMD, 256 registers each)
 //   128 rows: 8 x 1 (32-row blocks, two waves per SIMD, 256 registers each)
-// Score sums are split over 4 accumulator chains (2 in the 128-row kernel,
-// where registers are short).
+// Score sums are split over 4 accumulator chains where registers allow; the
+// two-waves-per-SIMD kernels spend their few spare registers on deeper LDS
+// read rings instead (measured: faster than two chains with shallower rings).
 int launch_decode(const DecodeArgs& a, int kv_dtype, int tile_class, int gx, int gy, int gz, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const bool fp8 = kv_dtype == MLA_KV_FP8_E4M3FN;
@@ -986,10 +987,10 @@ int launch_decode(const DecodeArgs& a, int kv_dtype, int tile_class, int gx, int
                        : launch_decode_t<false, 1, 2, 2, 1, 8, 8, 4>(a, gx, gy, gz, st);
     case 1: return fp8 ? launch_decode_t<true, 2, 2, 4, 1, 8, 8, 4>(a, gx, gy, gz, st)
                        : launch_decode_t<false, 2, 2, 2, 1, 8, 8, 4>(a, gx, gy, gz, st);
-    case 2: return fp8 ? launch_decode_t<true, 4, 2, 4, 2, 3, 3, 2>(a, gx, gy, gz, st)
+    case 2: return fp8 ? launch_decode_t<true, 4, 2, 4, 2, 5, 5, 1>(a, gx, gy, gz, st)
                        : launch_decode_t<false, 4, 2, 2, 2, 3, 3, 2>(a, gx, gy, gz, st);
-    case 3: return fp8 ? launch_decode_t<true, 8, 1, 8, 2, 3, 3, 2>(a, gx, gy, gz, st)
-                       : launch_decode_t<false, 8, 1, 4, 2, 3, 3, 2>(a, gx, gy, gz, st);
+    case 3: return fp8 ? launch_decode_t<true, 8, 1, 8, 2, 6, 6, 1>(a, gx, gy, gz, st)
+                       : launch_decode_t<false, 8, 1, 4, 2, 4, 3, 1>(a, gx, gy, gz, st);
   }
   return (int)hipErrorInvalidValue;
 }
