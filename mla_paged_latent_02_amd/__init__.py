@@ -11,6 +11,15 @@ import ctypes
 import os
 from typing import Optional
 
+# torch ships its own HIP runtime. Loaded first, it also serves this library
+# (same soname, libamdhip64.so.7); loaded after the library, it would bring a
+# second runtime into the process, and device pointers and the current device
+# of one would mean nothing to the other.
+try:
+    import torch  # noqa: F401
+except ImportError:  # C-only use: the library takes the system runtime
+    pass
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmla_decode.so")
 

@@ -141,3 +141,13 @@ def test_entry_points_reject_null_and_bad_plans_without_touching_the_device():
     assert lib.mla_decode(ctypes.byref(good), None, fake, fake, fake, fake, fake, None, fake,
                           good.ws_bytes, None) == 1
     assert lib.mla_split_combine(ctypes.byref(good), fake, 0, fake, None, None) == 3
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    # Importing the binding before torch must not map a second HIP runtime.
+    code = ("import mla_paged_latent_02_amd, torch\n"
+            "maps = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len({os.path.realpath(m) for m in maps}))")
+    out = subprocess.run([os.sys.executable, "-c", "import os\n" + code], cwd=ROOT, capture_output=True, text=True,
+                         check=True).stdout.split()
+    assert out[-1] == "1"
