@@ -34,6 +34,9 @@ typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2_t;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2_t;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
+typedef __attribute__((__vector_size__(2 * sizeof(short)))) short i16x2_t;
+typedef __attribute__((__vector_size__(2 * sizeof(unsigned short)))) unsigned short u16x2_t;
 
 #define LDS_PTR(T) __attribute__((address_space(3))) T*
 #ifndef MLA_STEP_BARRIER
@@ -630,17 +633,92 @@ void mla_decode_kernel(DecodeArgs a) {
   tile_row(a, b, grp, hw * 16 + i16, ctx, c_end, vis_end, row_out, row_ok);
 
   // ---- query fragments (B operand of S^T = K Q^T), resident for the whole chunk.
-  // bf16 cache: fragment t holds d = 32t + 8*g4 .. +7.
-  // fp8 cache:  fragment 2p+h holds d = 64p + 16*g4 + 8h .. +7 (one 16-byte LDS read of 16 fp8).
-  bf16x8_t qf[18];
+  // bf16 cache: qf[t] holds d = 32t + 8*g4 .. +7 (18 fragments).
+  // fp8 cache: the 512 latent dims run on the fp8 MFMA (16x16x128, 32 k per
+  // lane) over the raw cache bytes. For 128-dim block kb the lane's 32 bytes
+  // are d = 128kb + 16g4 + (0..15), then 128kb + 64 + 16g4 + (0..15): the dims
+  // of its two 16-byte LDS reads of a cache row. The bf16 query is written as
+  // 2^e (hi + 2^-4 lo), hi and lo fp8, with one e per head chosen so that the
+  // head's largest latent |q| lands in [128, 256); e reaches the MFMA through
+  // the E8M0 block scales of the head's column. (A lane's scale applies to a
+  // 32-wide k-block made of two lane groups' 16-byte halves, not to its own
+  // 32 bytes; one value for all four lanes of a column makes that moot.)
+  // hi keeps 4 of a bf16 value's 8 significant bits and the remainder has at
+  // most 4, so the split is exact for every element down to 2^-14 of the
+  // head's largest. The 64 rope dims stay on the bf16 MFMA: qf[h] holds
+  // d = 512 + 16g4 + 8h .. +7.
+  bf16x8_t qf[FP8 ? 2 : 18];
+  i32x8_t qh[FP8 ? 4 : 1], ql[FP8 ? 4 : 1];
+  int q_scale_hi = 127, q_scale_lo = 127;  // E8M0 block scales of the hi and lo terms
   {
     const uint16_t* qrow = a.q + (int64_t)row_out * kRowDim;
+    if constexpr (FP8) {
+      // raw[4kb + 2h + p] = d = 128kb + 64h + 16g4 + 8p .. +7
+      u32x4_t raw[16];
 #pragma unroll
-    for (int t = 0; t < 18; ++t) {
-      const int d = FP8 ? (64 * (t >> 1) + 16 * g4 + 8 * (t & 1)) : (32 * t + 8 * g4);
-      u32x4_t v = *(const u32x4_t*)(qrow + d);
-      if (!row_ok) v = u32x4_t{0, 0, 0, 0};
-      qf[t] = __builtin_bit_cast(bf16x8_t, v);
+      for (int t = 0; t < 16; ++t) {
+        u32x4_t v = *(const u32x4_t*)(qrow + 128 * (t >> 2) + 64 * ((t >> 1) & 1) + 16 * g4 + 8 * (t & 1));
+        if (!row_ok) v = u32x4_t{0, 0, 0, 0};
+        raw[t] = v;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        u32x4_t v = *(const u32x4_t*)(qrow + kLatentDim + 16 * g4 + 8 * h);
+        if (!row_ok) v = u32x4_t{0, 0, 0, 0};
+        qf[h] = __builtin_bit_cast(bf16x8_t, v);
+      }
+      // largest latent |q| of the lane (bf16 magnitudes order as their bit
+      // patterns), then of the head: lanes i16 + 16 {0, 1, 2, 3}
+      u16x2_t mx2 = u16x2_t{0, 0};
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(u16x2_t, raw[t][w] & 0x7fff7fffu));
+      const unsigned mx = mx2[0] > mx2[1] ? mx2[0] : mx2[1];
+      const float head_max = wave_max_16x4(__uint_as_float(mx << 16));
+      // exponent field E of the head's largest: |q| < 2^(E - 126). e = E - 134;
+      // E is raised to 11 so the lo scale stays >= 0 (such heads are all below 2^-115).
+      const int E = max((int)(__float_as_uint(head_max) >> 23), 11);
+      q_scale_hi = E - 7;   // 127 + e
+      q_scale_lo = E - 11;  // 127 + e - 4
+      const float inv = __uint_as_float((unsigned)(261 - E) << 23);  // 2^-e, exact
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int kbk = t >> 2, dw = 4 * ((t >> 1) & 1) + 2 * (t & 1);
+#pragma unroll
+        for (int w2 = 0; w2 < 2; ++w2) {
+          float xs[4];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const unsigned w = raw[t][2 * w2 + j];
+            xs[2 * j] = __uint_as_float(w << 16) * inv;
+            xs[2 * j + 1] = __uint_as_float(w & 0xffff0000u) * inv;
+          }
+          // |xs| < 256: in range of e4m3fn, which the converter does not saturate
+          i16x2_t hv = i16x2_t{0, 0};
+          hv = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hv, xs[0], xs[1], 1.0f, false);
+          hv = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hv, xs[2], xs[3], 1.0f, true);
+          const unsigned hw32 = __builtin_bit_cast(unsigned, hv);
+          const bf16x2_t h01 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hw32, 1.0f, false);
+          const bf16x2_t h23 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hw32, 1.0f, true);
+          // remainders times 16: exact, and again below 256 in magnitude
+          const float r0 = (xs[0] - (float)h01[0]) * 16.0f, r1 = (xs[1] - (float)h01[1]) * 16.0f;
+          const float r2 = (xs[2] - (float)h23[0]) * 16.0f, r3 = (xs[3] - (float)h23[1]) * 16.0f;
+          i16x2_t lv = i16x2_t{0, 0};
+          lv = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lv, r0, r1, 1.0f, false);
+          lv = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lv, r2, r3, 1.0f, true);
+          qh[kbk][dw + w2] = (int)hw32;
+          ql[kbk][dw + w2] = __builtin_bit_cast(int, lv);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 18; ++t) {
+        u32x4_t v = *(const u32x4_t*)(qrow + 32 * t + 8 * g4);
+        if (!row_ok) v = u32x4_t{0, 0, 0, 0};
+        qf[t] = __builtin_bit_cast(bf16x8_t, v);
+      }
     }
   }
 
@@ -687,9 +765,9 @@ void mla_decode_kernel(DecodeArgs a) {
     const int kv0 = c_start + blk * BN + kw * 32;
 
     // ---- S^T[kv, head] = K Q^T for the wave's 32 rows of the block (two tiles of 16 kv rows).
-    // The reads walk (step, tile) with a ring of KD reads in flight. Each tile's
-    // sum over the dims is split over QC accumulators (MFMA k-step c goes to
-    // chain c % QC) so that consecutive MFMAs do not wait on each other.
+    // The LDS reads run in a ring of KD units in flight. Each tile's sum over
+    // the dims is split over QC accumulators (the tile's m-th MFMA goes to chain
+    // m % QC) so that consecutive MFMAs do not wait on each other.
     f32x4_t sacc[2];
     {
       f32x4_t sch[2][QC];
@@ -697,33 +775,62 @@ void mla_decode_kernel(DecodeArgs a) {
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int c = 0; c < QC; ++c) sch[nt][c] = f32x4_t{0, 0, 0, 0};
-      constexpr int kSteps = FP8 ? 9 : 18;
-      constexpr int kMainSteps = FP8 ? 8 : 16;  // steps whose slots lie in the main region
-      constexpr int kReads = kSteps * 2;
-      u32x4_t kb[KD];
-      auto kread = [&](int i) -> u32x4_t {
-        const int step = i / 2, nt = i % 2;
-        if (step < kMainSteps)
-          return lds_b128(mstage, k_main_base + (uint32_t)(nt * 16 * L::kMainStride + step * 64));
-        const int s2 = 4 * (step - kMainSteps) + g4;  // logical tail slot of this lane
-        return lds_b128(tstage, (uint32_t)((nt * 16 + i16) * L::kTailBytes) + ((uint32_t)(s2 ^ L::tail_xor(i16)) << 4));
+      auto tail_read = [&](int nt, int slot) -> u32x4_t {  // logical 16-byte slot of the row's rope tail
+        return lds_b128(tstage, (uint32_t)((nt * 16 + i16) * L::kTailBytes) + ((uint32_t)(slot ^ L::tail_xor(i16)) << 4));
       };
+      if constexpr (FP8) {
+        // Unit u < 8 = (block kb = u / 2, tile nt = u % 2): the lane's two 16-byte
+        // reads of its row for block kb, one fp8 MFMA each for hi and lo.
+        // Units 8, 9 = the rope tail of tile 0, 1: one read, widened to bf16.
+        constexpr int kUnits = 10;
+        i32x8_t ku[KD];
+        auto kunit = [&](int u) -> i32x8_t {
+          if (u < 8) {
+            const uint32_t off = k_main_base + (uint32_t)((u & 1) * 16 * L::kMainStride + (u >> 1) * 128);
+            const u32x4_t lo = lds_b128(mstage, off), hi = lds_b128(mstage, off + 64);
+            return __builtin_bit_cast(i32x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+          const u32x4_t t = tail_read(u - 8, g4);
+          return __builtin_bit_cast(i32x8_t, __builtin_shufflevector(t, t, 0, 1, 2, 3, 0, 1, 2, 3));
+        };
 #pragma unroll
-      for (int i = 0; i < KD - 1; ++i) kb[i] = kread(i);
+        for (int u = 0; u < KD - 1; ++u) ku[u] = kunit(u);
 #pragma unroll
-      for (int i = 0; i < kReads; ++i) {
-        if (i + KD - 1 < kReads) kb[(i + KD - 1) % KD] = kread(i + KD - 1);
-        const u32x4_t raw = kb[i % KD];
-        const int step = i / 2, nt = i % 2;
-        if constexpr (FP8) {
-          // 16 fp8 = d in [64 step + 16 g4, +16): two k-steps of 8
-          const int c0 = (2 * step) % QC, c1 = (2 * step + 1) % QC;
-          sch[nt][c0] = mfma16(fp8x8_to_bf16x8(raw[0], raw[1]), qf[2 * step], sch[nt][c0]);
-          sch[nt][c1] = mfma16(fp8x8_to_bf16x8(raw[2], raw[3]), qf[2 * step + 1], sch[nt][c1]);
-        } else {
-          sch[nt][step % QC] = mfma16(__builtin_bit_cast(bf16x8_t, raw), qf[step], sch[nt][step % QC]);
+        for (int u = 0; u < kUnits; ++u) {
+          if (u + KD - 1 < kUnits) ku[(u + KD - 1) % KD] = kunit(u + KD - 1);
+          const i32x8_t k = ku[u % KD];
+          if (u < 8) {
+            const int kbk = u >> 1, nt = u & 1;
+            const int c0 = (2 * kbk) % QC, c1 = (2 * kbk + 1) % QC;
+            sch[nt][c0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, qh[kbk], sch[nt][c0], 0, 0, 0, 127, 0,
+                                                                            q_scale_hi);
+            sch[nt][c1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, ql[kbk], sch[nt][c1], 0, 0, 0, 127, 0,
+                                                                            q_scale_lo);
+          } else {
+            const int nt = u - 8, c0 = 8 % QC, c1 = 9 % QC;
+            sch[nt][c0] = mfma16(fp8x8_to_bf16x8((unsigned)k[0], (unsigned)k[1]), qf[0], sch[nt][c0]);
+            sch[nt][c1] = mfma16(fp8x8_to_bf16x8((unsigned)k[2], (unsigned)k[3]), qf[1], sch[nt][c1]);
+          }
+          MLA_STEP_BARRIER();
         }
-        MLA_STEP_BARRIER();
+      } else {
+        constexpr int kReads = 36;  // (step, tile): 16 main steps of 32 dims, then 2 tail steps
+        u32x4_t kb[KD];
+        auto kread = [&](int i) -> u32x4_t {
+          const int step = i / 2, nt = i % 2;
+          if (step < 16)
+            return lds_b128(mstage, k_main_base + (uint32_t)(nt * 16 * L::kMainStride + step * 64));
+          return tail_read(nt, 4 * (step - 16) + g4);
+        };
+#pragma unroll
+        for (int i = 0; i < KD - 1; ++i) kb[i] = kread(i);
+#pragma unroll
+        for (int i = 0; i < kReads; ++i) {
+          if (i + KD - 1 < kReads) kb[(i + KD - 1) % KD] = kread(i + KD - 1);
+          const int step = i / 2, nt = i % 2;
+          sch[nt][step % QC] = mfma16(__builtin_bit_cast(bf16x8_t, kb[i % KD]), qf[step], sch[nt][step % QC]);
+          MLA_STEP_BARRIER();
+        }
       }
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
@@ -976,20 +1083,21 @@ int launch_plan(const PlanArgs& a, void* stream) {
 //   32 rows:  2 x 2 (64-row blocks)
 //   64 rows:  4 x 2 (64-row blocks, two waves per SIMD, 256 registers each)
 //   128 rows: 8 x 1 (32-row blocks, two waves per SIMD, 256 registers each)
-// Score sums are split over 4 accumulator chains where registers allow; the
-// two-waves-per-SIMD kernels spend their few spare registers on deeper LDS
-// read rings instead (measured: faster than two chains with shallower rings).
+// Score sums are split over 4 accumulator chains where registers allow. For
+// the two-waves-per-SIMD kernels, ring depths are the deepest that keep every
+// register out of scratch inside the loop (measured: a single spill costs more
+// than any ring depth gains). For fp8, KD counts 32-byte units (two reads).
 int launch_decode(const DecodeArgs& a, int kv_dtype, int tile_class, int gx, int gy, int gz, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const bool fp8 = kv_dtype == MLA_KV_FP8_E4M3FN;
   switch (tile_class) {
-    case 0: return fp8 ? launch_decode_t<true, 1, 4, 2, 1, 8, 8, 4>(a, gx, gy, gz, st)
+    case 0: return fp8 ? launch_decode_t<true, 1, 4, 2, 1, 4, 8, 4>(a, gx, gy, gz, st)
                        : launch_decode_t<false, 1, 2, 2, 1, 8, 8, 4>(a, gx, gy, gz, st);
-    case 1: return fp8 ? launch_decode_t<true, 2, 2, 4, 1, 8, 8, 4>(a, gx, gy, gz, st)
+    case 1: return fp8 ? launch_decode_t<true, 2, 2, 4, 1, 4, 8, 4>(a, gx, gy, gz, st)
                        : launch_decode_t<false, 2, 2, 2, 1, 8, 8, 4>(a, gx, gy, gz, st);
-    case 2: return fp8 ? launch_decode_t<true, 4, 2, 4, 2, 5, 5, 1>(a, gx, gy, gz, st)
+    case 2: return fp8 ? launch_decode_t<true, 4, 2, 4, 2, 2, 3, 1>(a, gx, gy, gz, st)
                        : launch_decode_t<false, 4, 2, 2, 2, 3, 3, 2>(a, gx, gy, gz, st);
-    case 3: return fp8 ? launch_decode_t<true, 8, 1, 8, 2, 6, 6, 1>(a, gx, gy, gz, st)
+    case 3: return fp8 ? launch_decode_t<true, 8, 1, 8, 2, 3, 3, 1>(a, gx, gy, gz, st)
                        : launch_decode_t<false, 8, 1, 4, 2, 4, 3, 1>(a, gx, gy, gz, st);
   }
   return (int)hipErrorInvalidValue;
