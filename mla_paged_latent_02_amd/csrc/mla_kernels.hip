@@ -978,6 +978,80 @@ void mla_decode_kernel(DecodeArgs a) {
 // output of a chunk are loaded together. The streams are then merged through
 // LDS. CB shrinks when there are few rows to merge, so that many workgroups
 // share a long list of chunks.
+// Split-KV merge of one output row over N chunks (N known at compile time):
+// lane l holds columns 4l .. 4l+3 and 256 + 4l .. +3 (each load instruction
+// reads 1 KB of a row contiguously), every chunk's loads in flight at once.
+// Lane c < N reads chunk c's lse; M = max_c lse_c, w_c = 2^(lse_c - M),
+// out = sum_c w_c o_c / sum_c w_c, lse = (M + log2 sum_c w_c) ln 2.
+template <int N>
+__device__ __forceinline__ void merge_row(const CombineArgs& a, const float* src, int64_t rec_stride,
+                                          const float* lse_src, int64_t orow, int lane) {
+  f32x4_t x0[N], x1[N];
+#pragma unroll
+  for (int c = 0; c < N; ++c) {
+    x0[c] = *(const f32x4_t*)(src + c * rec_stride);
+    x1[c] = *(const f32x4_t*)(src + c * rec_stride + kLatentDim / 2);
+  }
+  const float lse_l = lane < N ? lse_src[lane * a.rows_per_group] : -__builtin_inff();
+  float M = lse_l;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  const float w_l = lse_l == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(lse_l - M);
+  float total = w_l;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) total += __shfl_xor(total, off);
+  f32x4_t acc0 = f32x4_t{0, 0, 0, 0}, acc1 = f32x4_t{0, 0, 0, 0};
+#pragma unroll
+  for (int c = 0; c < N; ++c) {
+    const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_l), c));
+    acc0 += w * x0[c];
+    acc1 += w * x1[c];
+  }
+  const float inv = total > 0.0f ? 1.0f / total : 0.0f;
+  u32x2_t lo, hi;
+  lo[0] = pack_bf16x2(acc0[0] * inv, acc0[1] * inv);
+  lo[1] = pack_bf16x2(acc0[2] * inv, acc0[3] * inv);
+  hi[0] = pack_bf16x2(acc1[0] * inv, acc1[1] * inv);
+  hi[1] = pack_bf16x2(acc1[2] * inv, acc1[3] * inv);
+  *(u32x2_t*)(a.out + orow * kLatentDim + 4 * lane) = lo;
+  *(u32x2_t*)(a.out + orow * kLatentDim + kLatentDim / 2 + 4 * lane) = hi;
+  if (a.lse && lane == 0) a.lse[orow] = total > 0.0f ? (M + __log2f(total)) * kLn2 : -__builtin_inff();
+}
+
+// Split-KV merge when no sequence has more than 8 chunks: one wave per output
+// row, dispatched on the row's chunk count, no LDS.
+__global__ __launch_bounds__(256) void mla_combine_rows_kernel(CombineArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int rows = a.rows_per_group;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keep the row scalar
+  const int64_t r = (int64_t)blockIdx.x * 4 + wave;
+  if (r >= (int64_t)a.batch * a.num_groups * rows) return;
+  const int bg = (int)(r / rows), rr = (int)(r - (int64_t)bg * rows);
+  const int b = bg / a.num_groups, grp = bg - b * a.num_groups;
+  const int n_b = a.nchunks[b];
+  if (n_b <= 1) return;
+  const int s = rr / a.heads_per_group;
+  const int head = grp * a.heads_per_group + rr % a.heads_per_group;
+  if (head >= a.num_heads) return;
+  const int64_t rec0 = (int64_t)a.partbase[b] + (int64_t)grp * n_b;
+  const int64_t rec_stride = (int64_t)rows * kLatentDim;
+  const float* src = a.part_out + (rec0 * rows + rr) * kLatentDim + 4 * lane;
+  const float* lse_src = a.part_lse + rec0 * rows + rr;
+  const int64_t orow = ((int64_t)b * a.seqlen_qo + s) * a.num_heads + head;
+  switch (n_b) {
+    case 2: merge_row<2>(a, src, rec_stride, lse_src, orow, lane); break;
+    case 3: merge_row<3>(a, src, rec_stride, lse_src, orow, lane); break;
+    case 4: merge_row<4>(a, src, rec_stride, lse_src, orow, lane); break;
+    case 5: merge_row<5>(a, src, rec_stride, lse_src, orow, lane); break;
+    case 6: merge_row<6>(a, src, rec_stride, lse_src, orow, lane); break;
+    case 7: merge_row<7>(a, src, rec_stride, lse_src, orow, lane); break;
+    case 8: merge_row<8>(a, src, rec_stride, lse_src, orow, lane); break;
+    default: break;  // the launcher only picks this kernel when max_chunks <= 8
+  }
+}
+
+// Split-KV merge for any chunk count: column blocks of CB, streams of threads
+// walking the chunks with a running max.
 template <int CB>
 __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
   constexpr int kThreadsPerChunk = CB / 4;
@@ -1103,13 +1177,21 @@ int launch_decode(const DecodeArgs& a, int kv_dtype, int tile_class, int gx, int
   return (int)hipErrorInvalidValue;
 }
 
+constexpr int kCombineRowsMaxChunks = 8;
+
 int launch_combine(const CombineArgs& a, int max_chunks, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const int rows = a.rows_per_group;
   const int gz = a.batch * a.num_groups;
-  // Narrow column blocks when few rows carry long chunk lists.
   const int64_t row_count = (int64_t)gz * rows;
-  if (row_count >= 1024 || max_chunks <= 8) {
+  if (max_chunks <= kCombineRowsMaxChunks) {
+    const int64_t wgs = (row_count + 3) / 4;
+    if (wgs > 0x7fffffff) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(mla_combine_rows_kernel, dim3((unsigned)wgs), dim3(256), 0, st, a);
+    return (int)hipGetLastError();
+  }
+  // Narrow column blocks when few rows carry long chunk lists.
+  if (row_count >= 1024) {
     hipLaunchKernelGGL(mla_combine_kernel<512>, dim3(1, rows, gz), dim3(256), 0, st, a);
   } else if (row_count >= 128) {
     hipLaunchKernelGGL(mla_combine_kernel<128>, dim3(kLatentDim / 128, rows, gz), dim3(256), 0, st, a);

@@ -66,7 +66,7 @@ void mla_plan_options_default(mla_plan_options_t* out) {
   if (!out) return;
   static const int32_t wg[4] = {1, 1, 1, 1};
   static const int32_t cmin[4] = {256, 256, 256, 1024};
-  static const int32_t cmax[4] = {8192, 8192, 4096, 4096};
+  static const int32_t cmax[4] = {8192, 8192, 4096, 6144};
   for (int c = 0; c < 4; ++c) {
     out->wg_per_cu[c] = wg[c];
     out->chunk_min[c] = cmin[c];

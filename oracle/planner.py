@@ -66,7 +66,7 @@ def _cdiv(a: int, b: int) -> int:
 class PlanOptions:
     wg_per_cu: List[int] = field(default_factory=lambda: [1, 1, 1, 1])
     chunk_min: List[int] = field(default_factory=lambda: [256, 256, 256, 1024])
-    chunk_max: List[int] = field(default_factory=lambda: [8192, 8192, 4096, 4096])
+    chunk_max: List[int] = field(default_factory=lambda: [8192, 8192, 4096, 6144])
     force_chunk: int = 0
 
 

@@ -132,6 +132,23 @@ def test_boundary_grid(kv_dtype, S, H, causal, P):
         assert_close(case, out, lse, label=f"grid force={force}")
 
 
+# merge paths: at most 8 chunks -> one wave per row; more -> column blocks of 16, 128 or 512
+# (by how many rows the batch has). Each case forces 64-row chunks so the merge sees many partials.
+@pytest.mark.parametrize("batch,heads,ctx,expect_many", [
+    (2, 128, [300, 64], False),                 # 5 chunks
+    (2, 12, [1000, 700], True),                 # 16 chunks, 24 rows
+    (3, 128, [1000, 700, 64], True),            # 16 chunks, 384 rows
+    (9, 128, [1100, 64, 700, 1, 900, 130, 1000, 65, 1024], True),  # 18 chunks, 1152 rows
+])
+def test_merge_paths(batch, heads, ctx, expect_many):
+    case = make_case(batch=batch, seqlen_qo=1, num_heads=heads, ctx=ctx, page_size=16, kv_dtype="fp8_e4m3fn",
+                     seed=90 + batch, pool_pages=sum(-(-c // 16) for c in ctx) + 2)
+    dec, out, lse = run(case, options(force_chunk=64))
+    check_plan_arrays(case, dec)
+    assert (dec.plan.max_chunks > 8) == expect_many
+    assert_close(case, out, lse, label=f"merge B={batch} H={heads}")
+
+
 def test_run_to_run_bitwise_determinism():
     case = make_case(batch=3, seqlen_qo=4, num_heads=16, ctx=[700, 5, 1300], page_size=16, kv_dtype="fp8_e4m3fn",
                      causal=True, seed=77)
@@ -140,6 +157,27 @@ def test_run_to_run_bitwise_determinism():
     _, o2, l2 = run(case, options(force_chunk=256), inputs=inp)
     assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
     assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
+
+
+def test_repeated_calls_on_one_workspace():
+    # one plan and workspace, three decode + combine calls: identical bits every time
+    from mla_paged_latent_02_amd.device import Decoder
+    case = make_case(batch=5, seqlen_qo=2, num_heads=32, ctx=[900, 2, 640, 1025, 333], page_size=16,
+                     kv_dtype="bf16", causal=True, seed=81)
+    dec = Decoder(upload(case), options(force_chunk=256), poison=True)
+    first = None
+    for _ in range(3):
+        dec.out.fill_(float("nan"))
+        dec.lse.fill_(float("nan"))
+        out, lse = dec()
+        torch.cuda.synchronize()
+        o, l = out.float().cpu().numpy(), lse.cpu().numpy()
+        if first is None:
+            first = (o, l)
+            assert_close(case, o, l, label="repeated calls")
+        else:
+            assert np.array_equal(o.view(np.uint32), first[0].view(np.uint32))
+            assert np.array_equal(l.view(np.uint32), first[1].view(np.uint32))
 
 
 def test_invalid_sequences_get_nan_rows_and_status_bits():

@@ -40,8 +40,9 @@ def test_plan_values_for_the_benchmark_shapes():
     # 16 heads x 4 tokens: want = floor(256 / 128) = 2 -> ceil(5200 / 2) = 2600 -> 2624 rows, 2 chunks
     p = reference_plan(128, 4, 16, 5200, 256)
     assert (p["heads_per_group"], p["tile_rows"], p["chunk_len"], p["max_chunks"]) == (16, 64, 2624, 2)
+    # 256 x 128 heads: want = 1 -> ceil(23333 / 1) rounds to 23360 -> capped at chunk_max = 6144, 4 chunks
     p = reference_plan(256, 1, 128, 23333, 256)
-    assert (p["chunk_len"], p["max_chunks"]) == (4096, 6)
+    assert (p["chunk_len"], p["max_chunks"]) == (6144, 4)
     # 12 heads, one sequence: want = 256 -> ceil(109440 / 256) = 428 -> 448 rows, 245 chunks
     p = reference_plan(1, 1, 12, 109440, 256)
     assert (p["tile_rows"], p["chunk_len"], p["max_chunks"]) == (16, 448, 245)
