@@ -32,7 +32,11 @@ and in 50-digit mpmath on tiny inputs, torch's float64 SDPA on gathered rows,
 closed forms (one row, constant V, zero query, two rows), invariants (page
 permutation, causal = truncation, split + LSE merge = unsplit, row duplication,
 head permutation, affine V), the fp8 decoder against torch on all 256 bytes, and
-the planner's structural invariants. No function here is "parity unpinned".
+the planner's structural invariants. The decode epilogue that produces the
+path's inputs (query concat and latent-cache insert, ``insert.py``) is pinned in
+``tests/test_oracle_insert.py``: encoders against torch's casts and hand-derived
+codes, rope against closed forms and a float64 complex product. No function here
+is "parity unpinned".
 """
 
 from .fp8 import E4M3FN_VALUES, decode_e4m3fn, bf16_bits_to_f64
@@ -48,6 +52,7 @@ from .attention import (
     mla_decode_reference_one,
 )
 from .planner import PlanOptions, reference_plan, device_plan_arrays, work_list
+from .insert import bf16_bits_to_f32, f32_to_bf16_rne, f32_to_e4m3fn, rope_f32, qcat_cache_insert_reference
 
 __all__ = [
     "E4M3FN_VALUES",
@@ -66,4 +71,9 @@ __all__ = [
     "reference_plan",
     "device_plan_arrays",
     "work_list",
+    "bf16_bits_to_f32",
+    "f32_to_bf16_rne",
+    "f32_to_e4m3fn",
+    "rope_f32",
+    "qcat_cache_insert_reference",
 ]
