@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 2
+#define MLA_ABI_VERSION 3
 #define MLA_ROW_DIM 576    /* q / cache row width: 512 latent + 64 rope */
 #define MLA_LATENT_DIM 512 /* V width = output width */
 #define MLA_MAX_SEQLEN_QO 8
@@ -211,6 +211,48 @@ mla_status_t mla_debug_read_plan_arrays(const mla_plan_t* plan, const void* d_wo
  */
 mla_status_t mla_debug_read_work_list(const mla_plan_t* plan, const void* d_workspace, int32_t* h_count,
                                       int32_t* h_items);
+
+/* ---- decode epilogue: query concat and latent-cache insert ---------------- */
+
+/* Bits mla_qcat_cache_insert may set in *d_status. */
+#define MLA_INSERT_SLOT_OUT_OF_RANGE 1u     /* slot_mapping[t] >= num_slots: that cache row is not written */
+#define MLA_INSERT_POSITION_OUT_OF_RANGE 2u /* positions[t] outside the rope table: not written either */
+
+typedef struct {
+  int32_t num_tokens;     /* T >= 0 */
+  int32_t num_heads;      /* H >= 1 query heads per token */
+  int32_t kv_dtype;       /* mla_kv_dtype_t of the cache */
+  float kv_scale;         /* fp8: stored = e4m3fn(value / kv_scale); bf16: must be 1 */
+  int64_t num_slots;      /* rows of the cache */
+  int32_t rope_positions; /* rows of the cos/sin table */
+  int32_t rope_neox;      /* 0: rope pairs (2i, 2i+1); 1: pairs (i, i + 32) */
+} mla_insert_params_t;
+
+/*
+ * The epilogue that produces mla_decode's inputs ("[Perf][Kimi-K3] Cut MLA
+ * decode concat/cache epilogue latency", Purpose: one fused kernel between the
+ * absorbed-query GEMM and decode attention, rows (token, head + 1)). For every
+ * token t:
+ *   q[t, h, 0:512] = ql_nope[t, h] and q[t, h, 512:576] = q_pe[t, h] (bit copy);
+ *   if slot_mapping[t] >= 0: cache row slot_mapping[t] = kv_c[t] | rope(k_pe[t]).
+ * Rope rotates 32 pairs, (2i, 2i+1) or with rope_neox (i, i + 32), by
+ * c = cos_sin[pos][i], s = cos_sin[pos][32 + i] with pos = positions[t]:
+ * x' = x c - y s, y' = y c + x s, float32 products then a float32 sum (no fused
+ * multiply-add). bf16 cache: round to nearest even; fp8 cache: e4m3fn of
+ * value / kv_scale (float32 division), saturated to +-448, nearest even, NaN
+ * -> 0x7f. The page prints no per-element arithmetic: these are this library's
+ * readings. One lane moves 16 bytes of a 576-wide row, 72 lanes per row.
+ *   d_ql_nope bf16 [T, H, 512]   d_q_pe bf16 [T, H, 64]   d_kv_c bf16 [T, 512]
+ *   d_k_pe bf16 [T, 64]          d_positions int32 [T]    d_cos_sin float [rope_positions, 64]
+ *   d_slot_mapping int64 [T]     d_q bf16 [T, H, 576]     d_cache [num_slots, 576] bf16 or fp8
+ *   d_status uint32 or NULL: MLA_INSERT_* bits are OR-ed in
+ * Every buffer is contiguous, 16-byte aligned and owned by the caller.
+ * Host-detectable errors return before any device work; T = 0 does nothing.
+ */
+mla_status_t mla_qcat_cache_insert(const mla_insert_params_t* params, const void* d_ql_nope, const void* d_q_pe,
+                                   const void* d_kv_c, const void* d_k_pe, const int32_t* d_positions,
+                                   const float* d_cos_sin, const int64_t* d_slot_mapping, void* d_q, void* d_cache,
+                                   uint32_t* d_status, void* stream);
 
 #ifdef __cplusplus
 }

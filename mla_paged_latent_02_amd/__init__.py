@@ -3,7 +3,7 @@
 Argument marshalling only: every step runs in the library's HIP kernels. The
 functions mirror the C entry points in include/mla_decode.h and take torch
 tensors for device buffers (torch supplies device memory and streams).
-The library must have been built (``python -m mla_paged_latent_02_amd.build``);
+The library must have been built (``python mla_paged_latent_02_amd/build.py``);
 importing this package without it raises ImportError.
 """
 
@@ -39,7 +39,10 @@ DEV_PAGE_OUT_OF_RANGE = 8
 # Every function the header declares, in declaration order.
 EXPORTED = ["mla_abi_version", "mla_status_string", "mla_plan_options_default", "mla_decode_plan_host",
             "mla_decode_workspace_size", "mla_decode_plan", "mla_decode", "mla_split_combine",
-            "mla_debug_read_plan_arrays", "mla_debug_read_work_list"]
+            "mla_debug_read_plan_arrays", "mla_debug_read_work_list", "mla_qcat_cache_insert"]
+
+INSERT_SLOT_OUT_OF_RANGE = 1
+INSERT_POSITION_OUT_OF_RANGE = 2
 
 
 class DecodeParams(ctypes.Structure):
@@ -52,6 +55,12 @@ class DecodeParams(ctypes.Structure):
 class PlanOptions(ctypes.Structure):
     _fields_ = [("wg_per_cu", ctypes.c_int32 * 4), ("chunk_min", ctypes.c_int32 * 4),
                 ("chunk_max", ctypes.c_int32 * 4), ("force_chunk", ctypes.c_int32)]
+
+
+class InsertParams(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("kv_scale", ctypes.c_float), ("num_slots", ctypes.c_int64), ("rope_positions", ctypes.c_int32),
+                ("rope_neox", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -74,7 +83,7 @@ class MlaError(RuntimeError):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m mla_paged_latent_02_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python mla_paged_latent_02_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P, V = ctypes.POINTER, ctypes.c_void_p
     sig = {
@@ -89,8 +98,12 @@ def _load():
         "mla_split_combine": ([P(Plan), V, ctypes.c_size_t, V, V, V], ctypes.c_int),
         "mla_debug_read_plan_arrays": ([P(Plan), V, V, V, V], ctypes.c_int),
         "mla_debug_read_work_list": ([P(Plan), V, V, V], ctypes.c_int),
+        "mla_qcat_cache_insert": ([P(InsertParams), V, V, V, V, V, V, V, V, V, V, V], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
+        if not hasattr(lib, name):
+            raise ImportError(f"{LIB_PATH} does not export {name}: it is older than this binding; "
+                              "rebuild it with `python mla_paged_latent_02_amd/build.py`")
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = res
@@ -183,6 +196,26 @@ def split_combine(plan: Plan, workspace, out, lse, stream=None):
                                 _ptr(out), _ptr(lse), _stream(stream))
     if st != MLA_OK:
         raise MlaError("mla_split_combine", st)
+
+
+def make_insert_params(*, num_tokens, num_heads, kv_dtype, kv_scale, num_slots, rope_positions,
+                       rope_neox) -> InsertParams:
+    p = InsertParams()
+    p.num_tokens, p.num_heads = int(num_tokens), int(num_heads)
+    p.kv_dtype = _KV_DTYPES[kv_dtype] if isinstance(kv_dtype, str) else int(kv_dtype)
+    p.kv_scale = float(kv_scale)
+    p.num_slots, p.rope_positions, p.rope_neox = int(num_slots), int(rope_positions), int(bool(rope_neox))
+    return p
+
+
+def qcat_cache_insert(params: InsertParams, ql_nope, q_pe, kv_c, k_pe, positions, cos_sin, slot_mapping, q, cache,
+                      status=None, stream=None):
+    """mla_qcat_cache_insert on torch device tensors (contiguous; bf16 data passed as any 2-byte dtype)."""
+    st = _lib.mla_qcat_cache_insert(ctypes.byref(params), _ptr(ql_nope), _ptr(q_pe), _ptr(kv_c), _ptr(k_pe),
+                                    _ptr(positions), _ptr(cos_sin), _ptr(slot_mapping), _ptr(q), _ptr(cache),
+                                    _ptr(status), _stream(stream))
+    if st != MLA_OK:
+        raise MlaError("mla_qcat_cache_insert", st)
 
 
 def read_plan_arrays(plan: Plan, workspace):

@@ -1,6 +1,6 @@
 """Builds libmla_decode.so (gfx950) in-tree with hipcc.
 
-    python -m mla_paged_latent_02_amd.build          # or build_library() from Python
+    python mla_paged_latent_02_amd/build.py    # by path: importing the package loads the library
 
 The library is the HIP kernels plus the C-ABI layer; nothing else is compiled.
 """
@@ -17,7 +17,7 @@ LIB_NAME = "libmla_decode.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["mla_kernels.hip", "mla_api.cpp", "mla_plan.cpp"]
+SOURCES = ["mla_kernels.hip", "mla_insert.hip", "mla_api.cpp", "mla_plan.cpp"]
 
 # Packed fp32 ops are kept off in device code: hipcc -O3 would otherwise form
 # v_pk_{add,mul,fma}_f32 from plain float code.

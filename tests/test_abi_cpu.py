@@ -32,6 +32,7 @@ def test_every_declared_symbol_is_exported():
 def test_struct_layouts_match_the_c_compiler(tmp_path):
     # sizeof/offsetof as gcc lays out the header, against the ctypes mirrors
     checks = [("mla_decode_params_t", mla.DecodeParams), ("mla_plan_options_t", mla.PlanOptions),
+              ("mla_insert_params_t", mla.InsertParams),
               ("mla_plan_t", mla.Plan)]
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "mla_decode.h"', "int main(void) {"]
     for cname, cls in checks:
@@ -151,3 +152,39 @@ def test_one_hip_runtime_whatever_the_import_order():
     out = subprocess.run([os.sys.executable, "-c", "import os\n" + code], cwd=ROOT, capture_output=True, text=True,
                          check=True).stdout.split()
     assert out[-1] == "1"
+
+
+def test_build_script_loads_without_the_package():
+    # __graft_entry__.build() loads the build script by path, so a missing or stale
+    # library cannot stop the build that would replace it
+    import importlib.util
+    import sys
+    spec = importlib.util.spec_from_file_location("_mla_build_check", os.path.join(ROOT, "mla_paged_latent_02_amd",
+                                                                                  "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    before = set(sys.modules)
+    spec.loader.exec_module(mod)
+    assert callable(mod.build_library) and "mla_insert.hip" in mod.SOURCES
+    assert not any(m.startswith("mla_paged_latent_02_amd") for m in set(sys.modules) - before)
+
+
+@pytest.mark.parametrize("bad, code", [
+    (dict(num_tokens=-1), 1), (dict(num_heads=0), 1), (dict(kv_dtype=5), 1), (dict(kv_scale=0.0), 1),
+    (dict(kv_scale=float("nan")), 1), (dict(kv_dtype="bf16", kv_scale=2.0), 1), (dict(num_slots=0), 1),
+    (dict(rope_positions=0), 1), (dict(rope_neox=2), 1),
+])
+def test_insert_rejects_bad_params_before_device_work(bad, code):
+    kw = dict(num_tokens=4, num_heads=8, kv_dtype="fp8_e4m3fn", kv_scale=0.5, num_slots=16, rope_positions=8,
+              rope_neox=0)
+    kw.update(bad)
+    p = mla.make_insert_params(**kw)
+    if "rope_neox" in bad:
+        p.rope_neox = bad["rope_neox"]
+    assert mla.lib().mla_qcat_cache_insert(p, *([None] * 11)) == code
+
+
+def test_insert_rejects_null_buffers():
+    p = mla.make_insert_params(num_tokens=4, num_heads=8, kv_dtype="bf16", kv_scale=1.0, num_slots=16,
+                               rope_positions=8, rope_neox=0)
+    assert mla.lib().mla_qcat_cache_insert(p, *([None] * 11)) == 1
+    assert mla.lib().mla_qcat_cache_insert(None, *([None] * 11)) == 1
