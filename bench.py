@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --copy-probe     (a plain 1 GiB device copy, to scale the HBM byte counters)
+    python bench.py --workload insert_t64_h8_fp8   (the decode epilogue: query concat + cache insert)
 
 One step = one call of the hot path (mla_decode + mla_split_combine) over the
 whole batch, inputs resident in HBM. Between steps a 1 GiB buffer is read
@@ -111,6 +112,78 @@ def cpu_baseline(case, min_s=10.0, max_s=30.0):
                       f"{secs:.1f} s), scaled by cache rows to one full call; float64 numpy, BLAS threads = {cores}"}
 
 
+def insert_bench(args):
+    """The decode epilogue (mla_qcat_cache_insert) on one workload: one call per step,
+    inputs resident, the same read flush between steps. Algorithmic bytes per call:
+    query parts read and written (T*H*576*2 each), latent rows read (T*576*2), one
+    rope-table row, position and slot per token, cache rows written (576*e per token
+    with a slot)."""
+    import numpy as np
+    import torch
+
+    import mla_paged_latent_02_amd as mla
+    import oracle
+    from mla_synth import INSERT_WORKLOADS, make_insert_case
+
+    c = make_insert_case(**INSERT_WORKLOADS[args.workload])
+    torch.cuda.set_device(0)
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to("cuda")
+
+    ins = [dev(x) for x in (c.ql_nope, c.q_pe, c.kv_c, c.k_pe, c.positions, c.cos_sin, c.slot_mapping)]
+    q = torch.empty((c.num_tokens, c.num_heads, 576), dtype=torch.int16, device="cuda")
+    cache = dev(c.cache)
+    p = mla.make_insert_params(num_tokens=c.num_tokens, num_heads=c.num_heads, kv_dtype=c.kv_dtype,
+                               kv_scale=c.kv_scale, num_slots=c.num_slots, rope_positions=c.rope_positions,
+                               rope_neox=c.neox)
+    stream = torch.cuda.current_stream()
+    flush = None if args.no_flush else torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    for _ in range(args.warmup):
+        mla.qcat_cache_insert(p, *ins, q, cache, None, stream)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        if flush is not None:
+            torch.sum(flush, dim=0, out=sink)
+        ev[k][0].record(stream)
+        mla.qcat_cache_insert(p, *ins, q, cache, None, stream)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    T, H = c.num_tokens, c.num_heads
+    e = 2 if c.kv_dtype == "bf16" else 1
+    written = int((c.slot_mapping >= 0).sum())
+    nbytes = 2 * T * H * 576 * 2 + T * 576 * 2 + T * (256 + 4 + 8) + written * 576 * e
+    us = float(np.mean(ms) * 1e3)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0, n = time.perf_counter(), 0
+        while time.perf_counter() - t0 < 10.0:
+            oracle.qcat_cache_insert_reference(c.ql_nope, c.q_pe, c.kv_c, c.k_pe, c.positions, c.cos_sin,
+                                               c.slot_mapping, c.cache, c.kv_dtype, c.kv_scale, c.neox)
+            n += 1
+        cpu = {"value": (time.perf_counter() - t0) / n * 1e6, "unit": "us", "cores": 1, "kind": "oracle",
+               "sample": f"{n} full calls of the numpy oracle (one thread, per-token loop), mean"}
+    print(json.dumps({
+        "metric": "MLA decode epilogue (query concat + latent-cache insert) µs/call", "value": us, "unit": "us",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": us / 1e3,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 query, " + ("bf16" if e == 2 else "fp8-e4m3fn") + " cache", "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": T, "heads": H, "kv_dtype": c.kv_dtype,
+                   "rope_neox": c.neox, "tokens_with_slot": written},
+        "call_us_p10_p50_p90": [float(np.percentile(ms, x) * 1e3) for x in (10, 50, 90)],
+        "flush_between_steps": flush is not None,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "mla_insert_kernel",
+                     "alg_bytes": nbytes, "note": "event pair around one launch; includes the launch gap"},
+        "cpu_baseline": cpu,
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +201,9 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+        return
+    if args.workload.startswith("insert_"):
+        insert_bench(args)
         return
 
     if not args.no_cpu_baseline:
@@ -226,7 +302,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if case.kv_dtype == "bf16" else "fp8-e4m3fn cache, bf16 mfma",
+        "dtype": "bf16" if case.kv_dtype == "bf16" else "fp8-e4m3fn cache: QK^T on fp8 MFMA, PV on bf16 MFMA",
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": case.batch, "heads": case.num_heads,
                    "seqlen_qo": case.seqlen_qo, "max_ctx": case.max_context_len, "page_size": case.page_size,
