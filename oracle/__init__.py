@@ -32,7 +32,8 @@ and in 50-digit mpmath on tiny inputs, torch's float64 SDPA on gathered rows,
 closed forms (one row, constant V, zero query, two rows), invariants (page
 permutation, causal = truncation, split + LSE merge = unsplit, row duplication,
 head permutation, affine V), the fp8 decoder against torch on all 256 bytes, and
-the planner's structural invariants. The decode epilogue that produces the
+the planner's structural invariants; the same invariants also run as hypothesis
+properties over random small shapes (``tests/test_oracle_properties.py``). The decode epilogue that produces the
 path's inputs (query concat and latent-cache insert, ``insert.py``) is pinned in
 ``tests/test_oracle_insert.py``: encoders against torch's casts and hand-derived
 codes, rope against closed forms and a float64 complex product. No function here
