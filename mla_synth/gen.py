@@ -134,6 +134,10 @@ WORKLOADS = {
                                      page_size=64, kv_dtype="fp8_e4m3fn", seed=3),
     "causal_mtp4_b128_h16_ctx5200_fp8_p16": dict(batch=128, seqlen_qo=4, num_heads=16, ctx=5200,
                                                  page_size=16, kv_dtype="fp8_e4m3fn", causal=True, seed=5),
+    # the dense shape with an fp8 cache: the shape and precision of the pages' MI355 table row
+    # (batch 64, ctx 8192, 128 heads, fp8 kernels), for comparison only
+    "dense_b64_h128_ctx8192_fp8": dict(batch=64, seqlen_qo=1, num_heads=128, ctx=8192, page_size=1,
+                                       kv_dtype="fp8_e4m3fn", seed=6),
 }
 for _b in range(1, 6):
     WORKLOADS[f"longctx_b{_b}_h12_ctx109440_fp8"] = dict(batch=_b, seqlen_qo=1, num_heads=12, ctx=109440,

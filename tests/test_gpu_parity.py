@@ -230,6 +230,10 @@ def test_dense_b64_h128_ctx8192_bf16_sampled():
     _sampled("dense_b64_h128_ctx8192_bf16", lambda c: [0, 1, 31, 62, 63])
 
 
+def test_dense_b64_h128_ctx8192_fp8_sampled():
+    _sampled("dense_b64_h128_ctx8192_fp8", lambda c: [0, 17, 63])
+
+
 def test_ragged_b256_h128_fp8_p64_sampled():
     def pick(c):
         order = np.argsort(c.context_lens)
