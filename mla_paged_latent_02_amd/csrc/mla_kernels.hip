@@ -371,13 +371,13 @@ struct BlockGather {
     return pg;
   }
   // main part of row r: one instruction; lane l fetches the row's 16-byte slot l
-  // (bf16: 64 slots; fp8: 32 slots, upper half of the wave idle)
+  // (bf16: 64 slots; fp8: 32 slots, the caller masks off the upper half of the wave)
   __device__ __forceinline__ void issue_main_row(int blk, int r, int slot_s) const {
     const uint32_t stage_off = (uint32_t)(blk % NS) * L::kBlockBytes;
     const uint8_t* src = cache + (int64_t)slot_s * L::kRowBytes + (lane << 4);
     const uint32_t dst =
         __builtin_amdgcn_readfirstlane(lds_base + stage_off + (uint32_t)((wave * RPW + r) * L::kMainStride));
-    if (FP8 ? lane < 32 : true) dma16(src, dst);
+    dma16(src, dst);
   }
   // rope tails: instruction m covers kTailRowsPerInst rows x kTailSlots slots;
   // sv is the slot of this lane's row
@@ -411,8 +411,10 @@ struct BlockGather {
       int q, rem;
       page_pos(row_kv(blk, my_row), q, rem);
       const int slot_v = checked(v_page) * P + rem;
+      if (FP8 ? lane < 32 : true) {
 #pragma unroll
-      for (int r = 0; r < RPW; ++r) issue_main_row(blk, r, __builtin_amdgcn_readlane(slot_v, r));
+        for (int r = 0; r < RPW; ++r) issue_main_row(blk, r, __builtin_amdgcn_readlane(slot_v, r));
+      }
 #pragma unroll
       for (int m = 0; m < kTailInsts; ++m)
         issue_tail(blk, m, __builtin_amdgcn_ds_bpermute((m * kTailRowsPerInst + trow) << 2, slot_v));
@@ -426,13 +428,28 @@ struct BlockGather {
 #pragma unroll
         for (int k = 0; k < 4; ++k) pid[r4 + k] = __builtin_amdgcn_readfirstlane((int)v[k]);
       }
+      // slots of the wave's rows; when one page holds them all (the rows are
+      // consecutive cache rows of a chunk), one lookup gives consecutive slots
       int slot[RPW];
+      const int kv_a = __builtin_amdgcn_readfirstlane(row_kv(blk, 0));
+      const int kv_b = __builtin_amdgcn_readfirstlane(row_kv(blk, RPW - 1));
+      int qa, rema;
+      page_pos(kv_a, qa, rema);
+      if (rema + (kv_b - kv_a) < P) {
+        const int s0 = checked(pid[0]) * P + rema;
 #pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        int q, rem;
-        page_pos(__builtin_amdgcn_readfirstlane(row_kv(blk, r)), q, rem);
-        slot[r] = checked(pid[r]) * P + rem;
-        issue_main_row(blk, r, slot[r]);
+        for (int r = 0; r < RPW; ++r) slot[r] = s0 + (__builtin_amdgcn_readfirstlane(row_kv(blk, r)) - kv_a);
+      } else {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+          int q, rem;
+          page_pos(__builtin_amdgcn_readfirstlane(row_kv(blk, r)), q, rem);
+          slot[r] = checked(pid[r]) * P + rem;
+        }
+      }
+      if (FP8 ? lane < 32 : true) {  // one exec mask for all the wave's main rows
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) issue_main_row(blk, r, slot[r]);
       }
 #pragma unroll
       for (int m = 0; m < kTailInsts; ++m) {
