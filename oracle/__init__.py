@@ -36,7 +36,10 @@ the planner's structural invariants; the same invariants also run as hypothesis
 properties over random small shapes (``tests/test_oracle_properties.py``). The decode epilogue that produces the
 path's inputs (query concat and latent-cache insert, ``insert.py``) is pinned in
 ``tests/test_oracle_insert.py``: encoders against torch's casts and hand-derived
-codes, rope against closed forms and a float64 complex product. No function here
+codes, rope against closed forms and a float64 complex product. The cached-prefix
+expansion of the latent into per-head K and V (``kv_b_proj.py``) is pinned in
+``tests/test_oracle_kv_b_proj.py``: selection matrices, brute force, head and page
+invariants, the fp8 scale and the rope part against torch's casts. No function here
 is "parity unpinned".
 """
 
@@ -54,6 +57,7 @@ from .attention import (
 )
 from .planner import PlanOptions, reference_plan, device_plan_arrays, work_list
 from .insert import bf16_bits_to_f32, f32_to_bf16_rne, f32_to_e4m3fn, rope_f32, qcat_cache_insert_reference
+from .kv_b_proj import gather_kv_b_proj_reference, output_rows, rope_bits
 
 __all__ = [
     "E4M3FN_VALUES",
@@ -77,4 +81,7 @@ __all__ = [
     "f32_to_e4m3fn",
     "rope_f32",
     "qcat_cache_insert_reference",
+    "gather_kv_b_proj_reference",
+    "output_rows",
+    "rope_bits",
 ]
