@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --copy-probe     (a plain 1 GiB device copy, to scale the HBM byte counters)
     python bench.py --workload insert_t64_h8_fp8   (the decode epilogue: query concat + cache insert)
+    python bench.py --workload kvb_b1_h12_ctx109440_fp8   (the cached-prefix gather_kv_b_proj)
 
 One step = one call of the hot path (mla_decode + mla_split_combine) over the
 whole batch, inputs resident in HBM. Between steps a 1 GiB buffer is read
@@ -184,6 +185,100 @@ def insert_bench(args):
     }), flush=True)
 
 
+# The pages' timings of this kernel on MI355X after the KV-chunk grid, in ms
+# ("perf(mla): chunk the non-FP4 gather_kv_b_proj over KV", ctx table).
+KVB_PAGE_MS = {4096: 0.038, 32000: 0.227, 65536: 0.442, 109440: 0.711}
+
+
+def kvb_bench(args):
+    """The cached-prefix expansion (mla_gather_kv_b_proj) on one workload: one call per
+    step, inputs resident, the same read flush between steps. Per call, over N cached
+    rows and H heads: algorithmic flops 2*N*H*256*512; algorithmic bytes N*576*e
+    (latent rows read once) + N*H*(192 + 128)*2 (K and V written) + H*256*512*2 (W)
+    + 4*(2B + 2 + pages) (page table and row offsets)."""
+    import numpy as np
+    import torch
+
+    import mla_paged_latent_02_amd as mla
+    import oracle
+    from mla_synth import KVB_WORKLOADS, make_kvb_case
+
+    c = make_kvb_case(name=args.workload, **KVB_WORKLOADS[args.workload])
+    torch.cuda.set_device(0)
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to("cuda")
+
+    N, H = c.total_rows, c.num_heads
+    ins = [dev(x) for x in (c.cache_raw, c.kv_indptr, c.kv_page_indices, c.cu_ctx, c.w_bits)]
+    k = torch.empty((N, H, 192), dtype=torch.int16, device="cuda")
+    v = torch.empty((N, H, 128), dtype=torch.int16, device="cuda")
+    p = mla.make_kv_b_proj_params(batch=c.batch, num_heads=H, page_size=c.page_size, kv_dtype=c.kv_dtype,
+                                  kv_scale=c.kv_scale, max_context_len=c.max_context_len, num_slots=c.num_slots,
+                                  num_out_rows=N)
+    stream = torch.cuda.current_stream()
+    flush = None if args.no_flush else torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    for _ in range(args.warmup):
+        mla.gather_kv_b_proj(p, *ins, k, v, None, stream)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        if flush is not None:
+            torch.sum(flush, dim=0, out=sink)
+        ev[s][0].record(stream)
+        mla.gather_kv_b_proj(p, *ins, k, v, None, stream)
+        ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    us = float(np.mean(ms) * 1e3)
+    e = 2 if c.kv_dtype == "bf16" else 1
+    flops = 2.0 * N * H * 256 * 512
+    nbytes = N * 576 * e + N * H * (192 + 128) * 2 + H * 256 * 512 * 2 + 4 * (2 * c.batch + 2 + len(c.kv_page_indices))
+    tf = flops / (us * 1e-6) / 1e12
+    gbs = nbytes / (us * 1e-6) / 1e9
+    t_mfma, t_hbm = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12), nbytes / (HBM_PEAK_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        roof = {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": tf / MFMA_BF16_PEAK_TFLOPS}
+    else:
+        roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}
+    roof.update({"traffic": None, "kernel": "mla_kv_b_proj_kernel", "alg_bytes": nbytes, "alg_flops": flops,
+                 "hbm_gbs": gbs, "note": "event pair around one launch; includes the launch gap"})
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0, done = time.perf_counter(), 0
+        while time.perf_counter() - t0 < 10.0 and done < N:
+            b0 = done
+            n = min(8192, N - b0)
+            rows = [r for r in oracle.output_rows(c.cu_ctx)[b0:b0 + n]]
+            oracle.gather_kv_b_proj_reference(c.cache_raw, c.kv_dtype, c.kv_scale, c.kv_indptr, c.kv_page_indices,
+                                              c.cu_ctx, c.page_size, c.w_bits, rows=[(b, r) for b, r, _ in rows])
+            done += n
+        el = time.perf_counter() - t0
+        cpu = {"value": el / done * N * 1e6, "unit": "us", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"first {done} of {N} cached rows through the numpy fp64 oracle (dgemm on all cores), "
+                         "time scaled to the full call"}
+    ctx = int(c.context_lens.max())
+    page_ms = KVB_PAGE_MS.get(ctx) if c.batch == 1 and c.page_size == 1 and H == 12 else None
+    print(json.dumps({
+        "metric": "MLA cached-prefix gather_kv_b_proj µs/call", "value": us, "unit": "us",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": us / 1e3,
+        "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": (us / (page_ms * 1e3)) if page_ms else None,
+        "pages_us_mi355x": page_ms * 1e3 if page_ms else None,
+        "dtype": ("bf16" if e == 2 else "fp8-e4m3fn") + " cache widened to bf16; bf16 MFMA, fp32 accumulation",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": c.batch, "heads": H, "cached_rows": N,
+                   "page_size": c.page_size, "kv_dtype": c.kv_dtype},
+        "call_us_p10_p50_p90": [float(np.percentile(ms, x) * 1e3) for x in (10, 50, 90)],
+        "flush_between_steps": flush is not None,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -204,6 +299,9 @@ def main():
         return
     if args.workload.startswith("insert_"):
         insert_bench(args)
+        return
+    if args.workload.startswith("kvb_"):
+        kvb_bench(args)
         return
 
     if not args.no_cpu_baseline:

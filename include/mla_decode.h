@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 3
+#define MLA_ABI_VERSION 4
 #define MLA_ROW_DIM 576    /* q / cache row width: 512 latent + 64 rope */
 #define MLA_LATENT_DIM 512 /* V width = output width */
 #define MLA_MAX_SEQLEN_QO 8
@@ -253,6 +253,52 @@ mla_status_t mla_qcat_cache_insert(const mla_insert_params_t* params, const void
                                    const void* d_kv_c, const void* d_k_pe, const int32_t* d_positions,
                                    const float* d_cos_sin, const int64_t* d_slot_mapping, void* d_q, void* d_cache,
                                    uint32_t* d_status, void* stream);
+
+/* ---- cached-prefix expansion: gather + kv_b_proj --------------------------- */
+
+/* Bits mla_gather_kv_b_proj may set in *d_status. */
+#define MLA_KVB_TOO_FEW_PAGES 1u      /* a row's page is past the sequence's page list: row read as zeros */
+#define MLA_KVB_SLOT_OUT_OF_RANGE 2u  /* a page id puts the row outside the cache: row read as zeros */
+#define MLA_KVB_ROWS_OUT_OF_RANGE 4u  /* cu_ctx[b] < 0, decreasing, or past num_out_rows: sequence not written */
+#define MLA_KVB_CTX_TOO_LONG 8u       /* a sequence is longer than max_context_len: rows past it not written */
+
+typedef struct {
+  int32_t batch;           /* B >= 0 sequences */
+  int32_t num_heads;       /* H >= 1 (local) heads of the projection */
+  int32_t page_size;       /* >= 1 cache rows per page */
+  int32_t kv_dtype;        /* mla_kv_dtype_t of the cache */
+  float kv_scale;          /* fp8: value = e4m3fn byte value * kv_scale; bf16: must be 1 */
+  int32_t max_context_len; /* >= every ctx_b; sizes the KV-chunk axis of the launch */
+  int64_t num_slots;       /* rows of the cache */
+  int64_t num_out_rows;    /* rows of d_k_out and d_v_out (>= cu_ctx[B]) */
+} mla_kv_b_proj_params_t;
+
+/*
+ * Expands the cached prefix of every sequence from the paged latent into full
+ * per-head K and V ("perf(mla): chunk the non-FP4 gather_kv_b_proj over KV",
+ * description: one program per (batch, head, KV chunk), chunks past a
+ * sequence's end exit at once). Sequence b has ctx_b = cu_ctx[b+1] - cu_ctx[b]
+ * cached rows; row r < ctx_b is cache slot
+ * kv_page_indices[kv_indptr[b] + r / page_size] * page_size + r % page_size,
+ * c = its first 512 values (times kv_scale for fp8), k_pe its last 64. For
+ * output row o = cu_ctx[b] + r and head h:
+ *   k[o, h, 0:128]   = W[h][0:128]   . c     (float32 accumulation, bf16 round to nearest even)
+ *   k[o, h, 128:192] = k_pe                  (bf16: bit copy; fp8: bf16(float(e4m3fn) * kv_scale))
+ *   v[o, h, 0:128]   = W[h][128:256] . c
+ * The page prints no formula: the reading is the standard MLA up-projection
+ * with W laid out as [H * 256, 512] (per head 128 K rows then 128 V rows).
+ *   d_kv_cache [num_slots, 576] bf16 or fp8   d_kv_indptr int32 [B + 1]
+ *   d_kv_page_indices int32 [kv_indptr[B]]     d_cu_ctx int32 [B + 1], cu_ctx[0] = 0 normally
+ *   d_w_kv_b bf16 [H, 256, 512]                d_k_out bf16 [num_out_rows, H, 192]
+ *   d_v_out bf16 [num_out_rows, H, 128]        d_status uint32 or NULL: MLA_KVB_* bits are OR-ed in
+ * Output rows that belong to no sequence are left untouched. Every buffer is
+ * contiguous, 16-byte aligned and owned by the caller. Host-detectable errors
+ * return before any device work; B = 0 or max_context_len = 0 does nothing.
+ */
+mla_status_t mla_gather_kv_b_proj(const mla_kv_b_proj_params_t* params, const void* d_kv_cache,
+                                  const int32_t* d_kv_indptr, const int32_t* d_kv_page_indices,
+                                  const int32_t* d_cu_ctx, const void* d_w_kv_b, void* d_k_out, void* d_v_out,
+                                  uint32_t* d_status, void* stream);
 
 #ifdef __cplusplus
 }

@@ -39,7 +39,8 @@ DEV_PAGE_OUT_OF_RANGE = 8
 # Every function the header declares, in declaration order.
 EXPORTED = ["mla_abi_version", "mla_status_string", "mla_plan_options_default", "mla_decode_plan_host",
             "mla_decode_workspace_size", "mla_decode_plan", "mla_decode", "mla_split_combine",
-            "mla_debug_read_plan_arrays", "mla_debug_read_work_list", "mla_qcat_cache_insert"]
+            "mla_debug_read_plan_arrays", "mla_debug_read_work_list", "mla_qcat_cache_insert",
+            "mla_gather_kv_b_proj"]
 
 INSERT_SLOT_OUT_OF_RANGE = 1
 INSERT_POSITION_OUT_OF_RANGE = 2
@@ -61,6 +62,12 @@ class InsertParams(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
                 ("kv_scale", ctypes.c_float), ("num_slots", ctypes.c_int64), ("rope_positions", ctypes.c_int32),
                 ("rope_neox", ctypes.c_int32)]
+
+
+class KvbParams(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32), ("kv_scale", ctypes.c_float), ("max_context_len", ctypes.c_int32),
+                ("num_slots", ctypes.c_int64), ("num_out_rows", ctypes.c_int64)]
 
 
 class Plan(ctypes.Structure):
@@ -99,6 +106,7 @@ def _load():
         "mla_debug_read_plan_arrays": ([P(Plan), V, V, V, V], ctypes.c_int),
         "mla_debug_read_work_list": ([P(Plan), V, V, V], ctypes.c_int),
         "mla_qcat_cache_insert": ([P(InsertParams), V, V, V, V, V, V, V, V, V, V, V], ctypes.c_int),
+        "mla_gather_kv_b_proj": ([P(KvbParams), V, V, V, V, V, V, V, V, V], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         if not hasattr(lib, name):
@@ -216,6 +224,26 @@ def qcat_cache_insert(params: InsertParams, ql_nope, q_pe, kv_c, k_pe, positions
                                     _ptr(status), _stream(stream))
     if st != MLA_OK:
         raise MlaError("mla_qcat_cache_insert", st)
+
+
+def make_kv_b_proj_params(*, batch, num_heads, page_size, kv_dtype, kv_scale, max_context_len, num_slots,
+                          num_out_rows) -> KvbParams:
+    p = KvbParams()
+    p.batch, p.num_heads, p.page_size = int(batch), int(num_heads), int(page_size)
+    p.kv_dtype = _KV_DTYPES[kv_dtype] if isinstance(kv_dtype, str) else int(kv_dtype)
+    p.kv_scale, p.max_context_len = float(kv_scale), int(max_context_len)
+    p.num_slots, p.num_out_rows = int(num_slots), int(num_out_rows)
+    return p
+
+
+def gather_kv_b_proj(params: KvbParams, kv_cache, kv_indptr, kv_page_indices, cu_ctx, w_kv_b, k_out, v_out,
+                     status=None, stream=None):
+    """mla_gather_kv_b_proj on torch device tensors (contiguous; bf16 data passed as any 2-byte dtype)."""
+    st = _lib.mla_gather_kv_b_proj(ctypes.byref(params), _ptr(kv_cache), _ptr(kv_indptr), _ptr(kv_page_indices),
+                                   _ptr(cu_ctx), _ptr(w_kv_b), _ptr(k_out), _ptr(v_out), _ptr(status),
+                                   _stream(stream))
+    if st != MLA_OK:
+        raise MlaError("mla_gather_kv_b_proj", st)
 
 
 def read_plan_arrays(plan: Plan, workspace):

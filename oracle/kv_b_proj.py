@@ -25,7 +25,7 @@ applied to the cached latent) is taken:
   compared bit for bit.
 
 Pins: ``tests/test_oracle_kv_b_proj.py`` (selection weights that turn the product
-into a known permutation of latent columns, linearity, head independence, page
+into a known permutation of latent columns, head independence, page
 permutation, the fp8 scale, the rope part against torch's own casts, a
 pure-Python brute force on tiny inputs).
 """
@@ -75,10 +75,13 @@ def gather_kv_b_proj_reference(cache_raw, kv_dtype, kv_scale, kv_indptr, kv_page
     if not rows:
         return np.zeros((0, H, NOPE_DIM)), np.zeros((0, H, ROPE), np.uint16), np.zeros((0, H, V_DIM))
     slots = np.empty(len(rows), np.int64)
+    seq_slots = {}  # the slots of every cached row of a sequence, gathered once per sequence
     for i, (b, r) in enumerate(rows):
         if not 0 <= r < cu[b + 1] - cu[b]:
             raise ValueError(f"row {r} is not a cached row of sequence {b}")
-        slots[i] = row_slots(kv_indptr, kv_page_indices, b, r + 1, page_size)[r]
+        if b not in seq_slots:
+            seq_slots[b] = row_slots(kv_indptr, kv_page_indices, b, int(cu[b + 1] - cu[b]), page_size)
+        slots[i] = seq_slots[b][r]
     raw = np.asarray(cache_raw)[slots]
     latent = dequantize_rows(raw, kv_dtype, kv_scale)[:, :LATENT]  # [N, 512]
     proj = (latent @ w.reshape(H * W_ROWS, LATENT).T).reshape(len(rows), H, W_ROWS)  # dgemm

@@ -33,6 +33,7 @@ def test_struct_layouts_match_the_c_compiler(tmp_path):
     # sizeof/offsetof as gcc lays out the header, against the ctypes mirrors
     checks = [("mla_decode_params_t", mla.DecodeParams), ("mla_plan_options_t", mla.PlanOptions),
               ("mla_insert_params_t", mla.InsertParams),
+              ("mla_kv_b_proj_params_t", mla.KvbParams),
               ("mla_plan_t", mla.Plan)]
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "mla_decode.h"', "int main(void) {"]
     for cname, cls in checks:
@@ -188,3 +189,27 @@ def test_insert_rejects_null_buffers():
                                rope_positions=8, rope_neox=0)
     assert mla.lib().mla_qcat_cache_insert(p, *([None] * 11)) == 1
     assert mla.lib().mla_qcat_cache_insert(None, *([None] * 11)) == 1
+
+
+@pytest.mark.parametrize("bad", [
+    dict(batch=-1), dict(num_heads=0), dict(page_size=0), dict(kv_dtype=7), dict(kv_scale=0.0),
+    dict(kv_scale=float("inf")), dict(kv_dtype="bf16", kv_scale=0.5), dict(max_context_len=-1), dict(num_slots=0),
+    dict(num_out_rows=-1),
+])
+def test_kv_b_proj_rejects_bad_params_before_device_work(bad):
+    kw = dict(batch=2, num_heads=12, page_size=1, kv_dtype="fp8_e4m3fn", kv_scale=0.5, max_context_len=100,
+              num_slots=1000, num_out_rows=200)
+    kw.update(bad)
+    p = mla.make_kv_b_proj_params(**kw)
+    assert mla.lib().mla_gather_kv_b_proj(p, *([None] * 9)) == 1
+
+
+def test_kv_b_proj_nulls_and_empty_calls():
+    kw = dict(batch=2, num_heads=12, page_size=1, kv_dtype="bf16", kv_scale=1.0, max_context_len=100,
+              num_slots=1000, num_out_rows=200)
+    assert mla.lib().mla_gather_kv_b_proj(mla.make_kv_b_proj_params(**kw), *([None] * 9)) == 1
+    assert mla.lib().mla_gather_kv_b_proj(None, *([None] * 9)) == 1
+    # nothing to do: returns before touching any buffer
+    assert mla.lib().mla_gather_kv_b_proj(mla.make_kv_b_proj_params(**dict(kw, batch=0)), *([None] * 9)) == 0
+    assert mla.lib().mla_gather_kv_b_proj(mla.make_kv_b_proj_params(**dict(kw, max_context_len=0)),
+                                          *([None] * 9)) == 0
