@@ -13,7 +13,8 @@
 //     LDS. An fp8 cache is widened to bf16 on the way (exactly: every e4m3fn
 //     value is a bf16 value); kv_scale multiplies the float32 result.
 //   * Wave w owns output rows 128 (w & 1) .. +127 of W[h] (so K or V) for the
-//     cached rows 64 (w >> 1) .. +63 of the chunk: 8 x 4 accumulator tiles.
+//     cached rows 64 (w >> 1) .. +63 of the chunk: 8 x 4 accumulator tiles,
+//     turned into whole output rows in LDS before they are stored.
 //   * Program ids are spread so that each XCD walks a contiguous run of them in
 //     (sequence, chunk, head) order: the heads of one chunk run back to back on
 //     one XCD and share its L2 copy of the latent rows.
@@ -43,6 +44,12 @@ constexpr int kRowBytes = kStageCols * 2;            // bf16 bytes of one row in
 constexpr int kWLdsBytes = kWRows * kRowBytes;       // 32 KB
 constexpr int kLatLdsBytes = kChunkRows * kRowBytes; // 16 KB
 constexpr int kXcds = 8;
+// Epilogue: each wave turns its 128 x 64 tile into bf16 rows of 256 bytes in LDS
+// (one row per cached row, 16 bytes of padding against bank conflicts), then
+// stores them 16 bytes per lane, 16 lanes per output row.
+constexpr int kEpRowBytes = kNope * 2 + 16;
+constexpr int kEpWaveBytes = 64 * kEpRowBytes;
+constexpr int kLdsBytes = (kWLdsBytes + kLatLdsBytes) > 4 * kEpWaveBytes ? (kWLdsBytes + kLatLdsBytes) : 4 * kEpWaveBytes;
 
 struct KvbArgs {
   const uint8_t* cache;
@@ -101,7 +108,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (r0 >= ctx) return;  // past this sequence's last chunk
   const int nrows = min(kChunkRows, ctx - r0);
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kWLdsBytes + kLatLdsBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
   KVB_LDS(uint8_t) w_lds = (KVB_LDS(uint8_t))lds;
   KVB_LDS(uint8_t) l_lds = w_lds + kWLdsBytes;
 
@@ -198,18 +205,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // acc[nb][tb][i]: W row nh*128 + nb*16 + 4g + i, cached row th*64 + tb*16 + l16
   const int H = a.num_heads;
+  __syncthreads();  // every wave is done with the last stage: LDS becomes the epilogue buffer
+  KVB_LDS(uint8_t) ep = (KVB_LDS(uint8_t))lds + wave * kEpWaveBytes;
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
-    const int t = th * 64 + tb * 16 + l16;
-    if (t >= nrows) continue;
-    const int64_t orow = (int64_t)row0 + r0 + t;
-    uint16_t* dst = nh == 0 ? a.k_out + (orow * H + h) * (kNope + kRope) : a.v_out + (orow * H + h) * kVDim;
+  for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
       const f32x4_t v = acc[nb][tb];
-      const u32x2_t p = {pack2(v[0] * a.kv_scale, v[1] * a.kv_scale), pack2(v[2] * a.kv_scale, v[3] * a.kv_scale)};
-      *(u32x2_t*)(dst + nb * 16 + 4 * g) = p;
+      *(KVB_LDS(u32x2_t))(ep + (tb * 16 + l16) * kEpRowBytes + (nb * 16 + 4 * g) * 2) =
+          u32x2_t{pack2(v[0] * a.kv_scale, v[1] * a.kv_scale), pack2(v[2] * a.kv_scale, v[3] * a.kv_scale)};
     }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int tr = i * 4 + (lane >> 4), piece = lane & 15;  // wave-local row, 16-byte piece of its 256 bytes
+    const int t = th * 64 + tr;
+    if (t >= nrows) continue;
+    const u32x4_t o = *(KVB_LDS(u32x4_t))(ep + tr * kEpRowBytes + piece * 16);
+    const int64_t orow = (int64_t)row0 + r0 + t;
+    uint16_t* dst = nh == 0 ? a.k_out + (orow * H + h) * (kNope + kRope) : a.v_out + (orow * H + h) * kVDim;
+    *(u32x4_t*)(dst + piece * 8) = o;
   }
 
   // rope part of K: 128 rows x 8 pieces of 8 values, 4 per thread
