@@ -17,6 +17,8 @@ Each part draws from its own stream ``default_rng([seed, part, ...])`` so that a
 part can be regenerated without the others.
 """
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 from typing import Optional
 
@@ -92,21 +94,32 @@ def make_case(*, batch, seqlen_qo, num_heads, ctx, page_size, kv_dtype, causal=F
     q = np.random.default_rng([seed, 0]).standard_normal((B, S, H, ROW), dtype=np.float32)
     q_bits = _to_bf16_bits(q)
 
+    # The pool is drawn in blocks of _GEN_ROWS rows, each from its own seeded stream, so the
+    # blocks can be drawn on several threads (numpy and torch fill without the GIL) and the
+    # bytes do not depend on the thread count.
     n_blocks = -(-num_slots // _GEN_ROWS)
     rows_of = lambda k: min(_GEN_ROWS, num_slots - k * _GEN_ROWS)
+    workers = max(1, min(8, len(os.sched_getaffinity(0)), n_blocks))
+
+    def each_block(fn):
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            return list(ex.map(fn, range(n_blocks)))
+
     if kv_dtype == "bf16":
         cache = np.empty((num_slots, ROW), np.uint16)
-        for k in range(n_blocks):
+
+        def fill_bf16(k):
             cache[k * _GEN_ROWS:k * _GEN_ROWS + rows_of(k)] = _to_bf16_bits(_pool_block(seed, k, rows_of(k)))
+        each_block(fill_bf16)
         kv_scale = 1.0
     elif kv_dtype == "fp8_e4m3fn":
-        amax = 0.0
-        for k in range(n_blocks):
-            amax = max(amax, float(np.abs(_pool_block(seed, k, rows_of(k))).max()))
+        amax = max([0.0] + each_block(lambda k: float(np.abs(_pool_block(seed, k, rows_of(k))).max())))
         scale = np.float32(amax / FP8_MAX) if amax > 0 else np.float32(1.0)
         cache = np.empty((num_slots, ROW), np.uint8)
-        for k in range(n_blocks):
+
+        def fill_fp8(k):
             cache[k * _GEN_ROWS:k * _GEN_ROWS + rows_of(k)] = _to_fp8_bytes(_pool_block(seed, k, rows_of(k)), scale)
+        each_block(fill_fp8)
         kv_scale = float(scale)
     else:
         raise ValueError(f"unknown kv dtype {kv_dtype!r}")
