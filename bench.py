@@ -14,7 +14,7 @@ write-back would compete with the next call's reads. Prints one JSON line.
 
 Roofline accounting (per decode launch):
   algorithmic bytes = sum_b ctx_b * 576 * e (each cache row read once; e = 2 bf16, 1 fp8)
-                      + B*S*H*576*2 (q) + B*S*H*512*2 (out) + 4*(B+1) + 4*pages + 4*B (page table, lengths)
+                      + B*S*H*576*eq (q; eq = 2 bf16, 1 fp8) + B*S*H*512*2 (out) + 4*(B+1) + 4*pages + 4*B (page table, lengths)
   algorithmic flops = 2 * H * (visible row visits) * (576 + 512)
 against 8 TB/s HBM and 2.5 PFLOP/s dense bf16 MFMA. roofline.traffic is the HBM
 rate implied by the rocprofv3 FETCH_SIZE + WRITE_SIZE counters of the decode
@@ -42,10 +42,11 @@ METRIC = "MLA decode µs/call + HBM TB/s & MFMA % peak, 128 heads ctx 8192 batch
 def algorithmic_counts(case):
     import numpy as np
     e = 2 if case.kv_dtype == "bf16" else 1
+    eq = 2 if case.q_dtype == "bf16" else 1
     ctx = case.context_lens.astype(np.int64)
     B, S, H = case.batch, case.seqlen_qo, case.num_heads
     rows = int(ctx.sum())
-    nbytes = rows * 576 * e + B * S * H * 576 * 2 + B * S * H * 512 * 2 + 4 * (B + 1) + 4 * int(case.kv_indptr[-1]) + 4 * B
+    nbytes = rows * 576 * e + B * S * H * 576 * eq + B * S * H * 512 * 2 + 4 * (B + 1) + 4 * int(case.kv_indptr[-1]) + 4 * B
     if case.causal:
         visits = int(sum(int(c) - S + 1 + s for c in ctx for s in range(S)))
     else:
@@ -106,7 +107,7 @@ def cpu_baseline(case, min_s=10.0, max_s=30.0):
         s0 = time.perf_counter()
         oracle.mla_decode_reference_one(case.q_bits, case.cache_raw, case.kv_dtype, case.kv_scale, case.kv_indptr,
                                         case.kv_page_indices, case.context_lens, case.page_size,
-                                        case.softmax_scale, case.causal, b)
+                                        case.softmax_scale, case.causal, b, q_scale=case.q_scale)
         secs += time.perf_counter() - s0
         rows_done += int(case.context_lens[b])
         evals += 1
@@ -330,7 +331,8 @@ def main():
         kv_page_indices=case.kv_page_indices, context_lens=case.context_lens, batch=case.batch,
         seqlen_qo=case.seqlen_qo, num_heads=case.num_heads, page_size=case.page_size,
         max_context_len=case.max_context_len, causal=case.causal, kv_dtype=case.kv_dtype,
-        softmax_scale=case.softmax_scale, kv_scale=case.kv_scale, num_slots=case.num_slots)
+        softmax_scale=case.softmax_scale, kv_scale=case.kv_scale, num_slots=case.num_slots,
+        q_dtype=case.q_dtype, q_scale=case.q_scale)
     stream = torch.cuda.current_stream()
     t0 = time.perf_counter()
     dec = Decoder(inp, None, 0, stream)
@@ -415,7 +417,9 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if case.kv_dtype == "bf16" else "fp8-e4m3fn cache: QK^T on fp8 MFMA, PV on bf16 MFMA",
+        "dtype": ("bf16" if case.kv_dtype == "bf16" else
+                  "fp8-e4m3fn query and cache: QK^T on fp8 MFMA, PV on bf16 MFMA" if case.q_dtype != "bf16" else
+                  "fp8-e4m3fn cache: QK^T on fp8 MFMA, PV on bf16 MFMA"),
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": case.batch, "heads": case.num_heads,
                    "seqlen_qo": case.seqlen_qo, "max_ctx": case.max_context_len, "page_size": case.page_size,

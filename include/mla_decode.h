@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 4
+#define MLA_ABI_VERSION 5
 #define MLA_ROW_DIM 576    /* q / cache row width: 512 latent + 64 rope */
 #define MLA_LATENT_DIM 512 /* V width = output width */
 #define MLA_MAX_SEQLEN_QO 8
@@ -67,6 +67,12 @@ typedef enum {
 } mla_status_t;
 
 typedef enum { MLA_KV_BF16 = 0, MLA_KV_FP8_E4M3FN = 1 } mla_kv_dtype_t;
+
+/* Query element type. fp8 is the pages' fp8-query x fp8-cache kernel setting
+ * ("HK MLA: MI35x m16x8 retune, new m16x4 kernel, page_size + mask support",
+ * the fp8_fp8 kernels of its file table): each query element is an e4m3fn
+ * byte times one per-tensor q_scale. It needs an fp8 cache. */
+typedef enum { MLA_Q_BF16 = 0, MLA_Q_FP8_E4M3FN = 1 } mla_q_dtype_t;
 
 /* Status-word bits written to the workspace by the device (see ws_status_offset). */
 #define MLA_DEV_CTX_TOO_SHORT 1u    /* context_lens[b] < seqlen_qo      */
@@ -86,6 +92,8 @@ typedef struct {
   float softmax_scale;     /* multiplies q . k */
   float kv_scale;          /* fp8: per-tensor dequant scale; bf16: must be 1 */
   int64_t num_slots;       /* rows in the cache pool; a multiple of page_size */
+  int32_t q_dtype;         /* mla_q_dtype_t; MLA_Q_FP8_E4M3FN needs kv_dtype MLA_KV_FP8_E4M3FN */
+  float q_scale;           /* fp8 query: per-tensor dequant scale; bf16 query: must be 1 */
 } mla_decode_params_t;
 
 /* Tunables of the work split, per tile class (tile rows 16, 32, 64, 128). */
@@ -170,7 +178,8 @@ mla_status_t mla_decode_plan(const mla_decode_params_t* params, const mla_plan_o
 /*
  * Decode attention over the paged cache. Workgroup x runs work item x / G for
  * head group x % G; workgroups past the item count exit at once.
- *   d_q              bf16 [B, S, H, 576], contiguous
+ *   d_q              [B, S, H, 576], contiguous: bf16, or e4m3fn bytes (value = byte * q_scale)
+ *                    when params.q_dtype is MLA_Q_FP8_E4M3FN
  *   d_kv_cache       [num_slots, 576] bf16 or fp8 e4m3fn bytes, contiguous
  *   d_kv_indptr      int32 [B+1]: page list of b is d_kv_page_indices[indptr[b] .. indptr[b+1])
  *   d_kv_page_indices int32 page ids (page p holds slots p*P .. p*P+P-1)

@@ -26,6 +26,7 @@ LIB_PATH = os.path.join(HERE, "libmla_decode.so")
 KV_BF16 = 0
 KV_FP8_E4M3FN = 1
 _KV_DTYPES = {"bf16": KV_BF16, "fp8_e4m3fn": KV_FP8_E4M3FN}
+_Q_DTYPES = {"bf16": 0, "fp8_e4m3fn": 1}  # mla_q_dtype_t
 
 MLA_OK = 0
 STATUS_NAMES = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED",
@@ -50,7 +51,7 @@ class DecodeParams(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seqlen_qo", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("max_context_len", ctypes.c_int32), ("causal", ctypes.c_int32),
                 ("kv_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("kv_scale", ctypes.c_float),
-                ("num_slots", ctypes.c_int64)]
+                ("num_slots", ctypes.c_int64), ("q_dtype", ctypes.c_int32), ("q_scale", ctypes.c_float)]
 
 
 class PlanOptions(ctypes.Structure):
@@ -130,11 +131,14 @@ def abi_version() -> int:
 
 
 def make_params(*, batch, seqlen_qo, num_heads, page_size, max_context_len, causal, kv_dtype, softmax_scale,
-                kv_scale, num_slots) -> DecodeParams:
+                kv_scale, num_slots, q_dtype="bf16", q_scale=1.0) -> DecodeParams:
     if isinstance(kv_dtype, str):
         kv_dtype = _KV_DTYPES[kv_dtype]
+    if isinstance(q_dtype, str):
+        q_dtype = _Q_DTYPES[q_dtype]
     return DecodeParams(int(batch), int(seqlen_qo), int(num_heads), int(page_size), int(max_context_len),
-                        int(causal), int(kv_dtype), float(softmax_scale), float(kv_scale), int(num_slots))
+                        int(causal), int(kv_dtype), float(softmax_scale), float(kv_scale), int(num_slots),
+                        int(q_dtype), float(q_scale))
 
 
 def default_options() -> PlanOptions:

@@ -78,9 +78,12 @@ mla_status_t mla_decode(const mla_plan_t* plan, const void* d_q, const void* d_k
   a.rows_per_group = plan->rows_per_group;
   a.chunk_len = plan->chunk_len;
   a.causal = p.causal;
-  a.score_scale_log2 = float(double(p.softmax_scale) * double(p.kv_scale) * 1.4426950408889634);
+  // both per-tensor scales multiply every score: folded into the softmax scale
+  a.score_scale_log2 =
+      float(double(p.softmax_scale) * double(p.kv_scale) * double(p.q_scale) * 1.4426950408889634);
   a.out_scale = p.kv_scale;
-  if (mla::launch_decode(a, p.kv_dtype, plan->tile_class, plan->grid[0], plan->grid[1], plan->grid[2], stream) != 0)
+  if (mla::launch_decode(a, p.kv_dtype, p.q_dtype == MLA_Q_FP8_E4M3FN, plan->tile_class, plan->grid[0],
+                         plan->grid[1], plan->grid[2], stream) != 0)
     return MLA_ERR_HIP;
   return MLA_OK;
 }

@@ -15,7 +15,7 @@ constexpr int kMaxSeqlenQo = MLA_MAX_SEQLEN_QO;
 
 // Everything one decode launch needs, passed by value.
 struct DecodeArgs {
-  const uint16_t* q;            // bf16 [B, S, H, 576]
+  const uint16_t* q;            // [B, S, H, 576]: bf16, or e4m3fn bytes (fp8 query)
   const uint8_t* cache;         // [num_slots, 576] elements of 2 (bf16) or 1 (fp8) bytes
   const int32_t* kv_indptr;     // [B+1]
   const int32_t* kv_page_indices;
@@ -60,7 +60,7 @@ struct PlanArgs {
 
 // Launchers (mla_kernels.hip). Return hipError_t as int.
 int launch_plan(const PlanArgs& a, void* stream);
-int launch_decode(const DecodeArgs& a, int kv_dtype, int tile_class, int grid_x, int grid_y, int grid_z,
+int launch_decode(const DecodeArgs& a, int kv_dtype, bool q_fp8, int tile_class, int grid_x, int grid_y, int grid_z,
                   void* stream);
 int launch_combine(const CombineArgs& a, int max_chunks, void* stream);
 

@@ -613,9 +613,13 @@ struct DecodeCfg {
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
-template <bool FP8, int HW, int KW, int NS, int WPE, int KD, int VD, int QC>
+// QF8 (fp8 cache only): the query is e4m3fn bytes; its latent dims go to the
+// fp8 MFMA as they are (one term, unit block scale; the per-tensor q scale is
+// folded into the softmax scale) and its rope dims are widened exactly to bf16.
+template <bool FP8, int HW, int KW, int NS, int WPE, int KD, int VD, int QC, bool QF8 = false>
 __global__ __launch_bounds__(HW * KW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void mla_decode_kernel(DecodeArgs a) {
+  static_assert(FP8 || !QF8, "an fp8 query needs an fp8 cache");
   using Cfg = DecodeCfg<FP8, HW, KW, NS>;
   using L = typename Cfg::L;
   constexpr int NW = Cfg::kWaves;
@@ -667,7 +671,23 @@ void mla_decode_kernel(DecodeArgs a) {
   bf16x8_t qf[FP8 ? 2 : 18];
   i32x8_t qh[FP8 ? 4 : 1], ql[FP8 ? 4 : 1];
   int q_scale_hi = 127, q_scale_lo = 127;  // E8M0 block scales of the hi and lo terms
-  {
+  if constexpr (QF8) {
+    // qh[kb]: bytes 0..15 = d = 128kb + 16g4 + (0..15), bytes 16..31 = 128kb + 64 + 16g4 + (0..15)
+    const uint8_t* qrow8 = reinterpret_cast<const uint8_t*>(a.q) + (int64_t)row_out * kRowDim;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      u32x4_t lo = *(const u32x4_t*)(qrow8 + 128 * kb + 16 * g4);
+      u32x4_t hi = *(const u32x4_t*)(qrow8 + 128 * kb + 64 + 16 * g4);
+      if (!row_ok) lo = hi = u32x4_t{0, 0, 0, 0};
+      qh[kb] = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x2_t w = *(const u32x2_t*)(qrow8 + kLatentDim + 16 * g4 + 8 * h);
+      if (!row_ok) w = u32x2_t{0, 0};
+      qf[h] = fp8x8_to_bf16x8(w[0], w[1]);
+    }
+  } else {
     const uint16_t* qrow = a.q + (int64_t)row_out * kRowDim;
     if constexpr (FP8) {
       // raw[4kb + 2h + p] = d = 128kb + 64h + 16g4 + 8p .. +7
@@ -821,8 +841,9 @@ void mla_decode_kernel(DecodeArgs a) {
             const int c0 = (2 * kbk) % QC, c1 = (2 * kbk + 1) % QC;
             sch[nt][c0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, qh[kbk], sch[nt][c0], 0, 0, 0, 127, 0,
                                                                             q_scale_hi);
-            sch[nt][c1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, ql[kbk], sch[nt][c1], 0, 0, 0, 127, 0,
-                                                                            q_scale_lo);
+            if constexpr (!QF8)
+              sch[nt][c1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, ql[kbk], sch[nt][c1], 0, 0, 0, 127,
+                                                                              0, q_scale_lo);
           } else {
             const int nt = u - 8, c0 = 8 % QC, c1 = 9 % QC;
             sch[nt][c0] = mfma16(fp8x8_to_bf16x8((unsigned)k[0], (unsigned)k[1]), qf[0], sch[nt][c0]);
@@ -1154,9 +1175,9 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
   }
 }
 
-template <bool FP8, int HW, int KW, int NS, int WPE, int KD, int VD, int QC>
+template <bool FP8, int HW, int KW, int NS, int WPE, int KD, int VD, int QC, bool QF8 = false>
 int launch_decode_t(const DecodeArgs& a, int gx, int gy, int gz, hipStream_t st) {
-  hipLaunchKernelGGL((mla_decode_kernel<FP8, HW, KW, NS, WPE, KD, VD, QC>), dim3(gx, gy, gz), dim3(HW * KW * 64), 0,
+  hipLaunchKernelGGL((mla_decode_kernel<FP8, HW, KW, NS, WPE, KD, VD, QC, QF8>), dim3(gx, gy, gz), dim3(HW * KW * 64), 0,
                      st, a);
   return (int)hipGetLastError();
 }
@@ -1178,9 +1199,20 @@ int launch_plan(const PlanArgs& a, void* stream) {
 // the two-waves-per-SIMD kernels, ring depths are the deepest that keep every
 // register out of scratch inside the loop (measured: a single spill costs more
 // than any ring depth gains). For fp8, KD counts 32-byte units (two reads).
-int launch_decode(const DecodeArgs& a, int kv_dtype, int tile_class, int gx, int gy, int gz, void* stream) {
+int launch_decode(const DecodeArgs& a, int kv_dtype, bool q_fp8, int tile_class, int gx, int gy, int gz,
+                  void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const bool fp8 = kv_dtype == MLA_KV_FP8_E4M3FN;
+  if (q_fp8) {  // fp8 query x fp8 cache: the fp8-cache configurations
+    if (!fp8) return (int)hipErrorInvalidValue;
+    switch (tile_class) {
+      case 0: return launch_decode_t<true, 1, 4, 2, 1, 4, 8, 4, true>(a, gx, gy, gz, st);
+      case 1: return launch_decode_t<true, 2, 2, 4, 1, 4, 8, 4, true>(a, gx, gy, gz, st);
+      case 2: return launch_decode_t<true, 4, 2, 4, 2, 2, 3, 1, true>(a, gx, gy, gz, st);
+      case 3: return launch_decode_t<true, 8, 1, 8, 2, 3, 3, 1, true>(a, gx, gy, gz, st);
+    }
+    return (int)hipErrorInvalidValue;
+  }
   switch (tile_class) {
     case 0: return fp8 ? launch_decode_t<true, 1, 4, 2, 1, 4, 8, 4>(a, gx, gy, gz, st)
                        : launch_decode_t<false, 1, 2, 2, 1, 8, 8, 4>(a, gx, gy, gz, st);

@@ -63,7 +63,7 @@ struct KvbArgs {
   int64_t num_slots;
   int64_t num_out_rows;
   int64_t programs;   // batch * chunks * heads
-  int32_t num_heads, page_size, chunks;
+  int32_t num_heads, page_size, chunks, max_ctx;
   float kv_scale;
 };
 
@@ -103,10 +103,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (chunk == 0 && h == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, MLA_KVB_ROWS_OUT_OF_RANGE);
     return;
   }
-  if (chunk == 0 && h == 0 && threadIdx.x == 0 && ctx > a.chunks * kChunkRows && a.status)
+  if (chunk == 0 && h == 0 && threadIdx.x == 0 && ctx > a.max_ctx && a.status)
     atomicOr(a.status, MLA_KVB_CTX_TOO_LONG);  // rows past max_context_len are not written
-  if (r0 >= ctx) return;  // past this sequence's last chunk
-  const int nrows = min(kChunkRows, ctx - r0);
+  const int lim = min(ctx, a.max_ctx);         // rows of this sequence that are expanded
+  if (r0 >= lim) return;                       // past this sequence's last chunk
+  const int nrows = min(kChunkRows, lim - r0);
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
   KVB_LDS(uint8_t) w_lds = (KVB_LDS(uint8_t))lds;
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int i = 0; i < kMyRows; ++i) {
     const int r = r0 + my_row0 + kRowStep * i;
     src[i] = nullptr;
-    if (r < ctx) {
+    if (r < lim) {
       const int q = r / a.page_size;
       if (pg_first + q >= pg_end) {
         bad |= MLA_KVB_TOO_FEW_PAGES;
@@ -295,6 +296,7 @@ extern "C" mla_status_t mla_gather_kv_b_proj(const mla_kv_b_proj_params_t* p, co
   a.num_heads = p->num_heads;
   a.page_size = p->page_size;
   a.chunks = (int32_t)chunks;
+  a.max_ctx = p->max_context_len;
   a.kv_scale = p->kv_scale;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 g((unsigned)grid), blk(256);

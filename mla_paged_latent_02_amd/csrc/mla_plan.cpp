@@ -40,6 +40,10 @@ mla_status_t validate_params(const mla_decode_params_t& p) {
   if (!std::isfinite(p.kv_scale) || !(p.kv_scale > 0.0f)) return MLA_ERR_INVALID_ARG;
   if (p.kv_dtype == MLA_KV_BF16 && p.kv_scale != 1.0f) return MLA_ERR_INVALID_ARG;
   if (p.num_slots < 1 || p.num_slots % p.page_size) return MLA_ERR_INVALID_ARG;
+  if (p.q_dtype != MLA_Q_BF16 && p.q_dtype != MLA_Q_FP8_E4M3FN) return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(p.q_scale) || !(p.q_scale > 0.0f)) return MLA_ERR_INVALID_ARG;
+  if (p.q_dtype == MLA_Q_BF16 && p.q_scale != 1.0f) return MLA_ERR_INVALID_ARG;
+  if (p.q_dtype == MLA_Q_FP8_E4M3FN && p.kv_dtype != MLA_KV_FP8_E4M3FN) return MLA_ERR_UNSUPPORTED;
   if (p.batch > 65535) return MLA_ERR_UNSUPPORTED;  // grid z limit
   return MLA_OK;
 }

@@ -23,12 +23,16 @@ class DeviceInputs:
     @staticmethod
     def from_host(*, q_bits, cache_raw, kv_indptr, kv_page_indices, context_lens, batch, seqlen_qo, num_heads,
                   page_size, max_context_len, causal, kv_dtype, softmax_scale, kv_scale, num_slots,
-                  device="cuda") -> "DeviceInputs":
-        q = torch.from_numpy(np.ascontiguousarray(q_bits).view(np.int16)).view(torch.bfloat16).to(device)
+                  q_dtype="bf16", q_scale=1.0, device="cuda") -> "DeviceInputs":
+        if q_dtype == "bf16":
+            q = torch.from_numpy(np.ascontiguousarray(q_bits).view(np.int16)).view(torch.bfloat16).to(device)
+        else:  # e4m3fn bytes
+            q = torch.from_numpy(np.ascontiguousarray(q_bits).view(np.uint8)).to(device)
         cache = torch.from_numpy(np.ascontiguousarray(cache_raw).view(np.uint8)).to(device)
         params = make_params(batch=batch, seqlen_qo=seqlen_qo, num_heads=num_heads, page_size=page_size,
                              max_context_len=max_context_len, causal=causal, kv_dtype=kv_dtype,
-                             softmax_scale=softmax_scale, kv_scale=kv_scale, num_slots=num_slots)
+                             softmax_scale=softmax_scale, kv_scale=kv_scale, num_slots=num_slots,
+                             q_dtype=q_dtype, q_scale=q_scale)
         return DeviceInputs(
             q=q, cache=cache,
             kv_indptr=torch.from_numpy(np.ascontiguousarray(kv_indptr, dtype=np.int32)).to(device),

@@ -43,11 +43,13 @@ class MlaCase:
     kv_scale: float
     max_context_len: int
     num_slots: int
-    q_bits: np.ndarray  # uint16 [B, S, H, 576]
+    q_bits: np.ndarray  # [B, S, H, 576]: uint16 (bf16) or uint8 (fp8 e4m3fn bytes)
     cache_raw: np.ndarray  # uint16 [num_slots, 576] (bf16) or uint8 (fp8)
     kv_indptr: np.ndarray  # int32 [B + 1]
     kv_page_indices: np.ndarray  # int32 [total pages]
     context_lens: np.ndarray  # int32 [B]
+    q_dtype: str = "bf16"  # or "fp8_e4m3fn": query value = byte * q_scale
+    q_scale: float = 1.0
 
     @property
     def kv_bytes_per_elem(self) -> int:
@@ -71,7 +73,7 @@ def _pool_block(seed: int, block: int, rows: int) -> np.ndarray:
 
 def make_case(*, batch, seqlen_qo, num_heads, ctx, page_size, kv_dtype, causal=False, seed=0,
               pool_pages: Optional[int] = None, softmax_scale: float = 1.0 / np.sqrt(192.0),
-              name: str = "case", max_context_len: Optional[int] = None) -> MlaCase:
+              name: str = "case", max_context_len: Optional[int] = None, q_dtype: str = "bf16") -> MlaCase:
     """Build one seeded case. ``ctx`` is an int, a list of ints, or ("uniform", lo, hi)."""
     B, S, H, P = int(batch), int(seqlen_qo), int(num_heads), int(page_size)
     if isinstance(ctx, tuple) and ctx and ctx[0] == "uniform":
@@ -92,7 +94,14 @@ def make_case(*, batch, seqlen_qo, num_heads, ctx, page_size, kv_dtype, causal=F
     num_slots = num_pages * P
 
     q = np.random.default_rng([seed, 0]).standard_normal((B, S, H, ROW), dtype=np.float32)
-    q_bits = _to_bf16_bits(q)
+    if q_dtype == "bf16":
+        q_bits, q_scale = _to_bf16_bits(q), 1.0
+    elif q_dtype == "fp8_e4m3fn":  # the same per-tensor recipe as the cache: scale = amax / 448
+        amax = float(np.abs(q).max())
+        q_scale = np.float32(amax / FP8_MAX) if amax > 0 else np.float32(1.0)
+        q_bits, q_scale = _to_fp8_bytes(q, q_scale), float(q_scale)
+    else:
+        raise ValueError(f"unknown query dtype {q_dtype!r}")
 
     # The pool is drawn in blocks of _GEN_ROWS rows, each from its own seeded stream, so the
     # blocks can be drawn on several threads (numpy and torch fill without the GIL) and the
@@ -129,7 +138,7 @@ def make_case(*, batch, seqlen_qo, num_heads, ctx, page_size, kv_dtype, causal=F
         kv_dtype=kv_dtype, softmax_scale=float(np.float32(softmax_scale)), kv_scale=kv_scale,
         max_context_len=int(max_context_len if max_context_len is not None else lens.max()),
         num_slots=num_slots, q_bits=q_bits, cache_raw=cache, kv_indptr=kv_indptr,
-        kv_page_indices=kv_page_indices, context_lens=lens.astype(np.int32))
+        kv_page_indices=kv_page_indices, context_lens=lens.astype(np.int32), q_dtype=q_dtype, q_scale=q_scale)
 
 
 # The workloads, named by what they are. Sizes follow the decode shapes the pages
@@ -151,6 +160,9 @@ WORKLOADS = {
     # (batch 64, ctx 8192, 128 heads, fp8 kernels), for comparison only
     "dense_b64_h128_ctx8192_fp8": dict(batch=64, seqlen_qo=1, num_heads=128, ctx=8192, page_size=1,
                                        kv_dtype="fp8_e4m3fn", seed=6),
+    # the same shape with an fp8 query as well: the fp8_fp8 kernels of the HK page's file table
+    "dense_b64_h128_ctx8192_fp8q": dict(batch=64, seqlen_qo=1, num_heads=128, ctx=8192, page_size=1,
+                                        kv_dtype="fp8_e4m3fn", q_dtype="fp8_e4m3fn", seed=7),
 }
 for _b in range(1, 6):
     WORKLOADS[f"longctx_b{_b}_h12_ctx109440_fp8"] = dict(batch=_b, seqlen_qo=1, num_heads=12, ctx=109440,

@@ -50,6 +50,7 @@ from .attention import (
     ROW_DIM,
     row_slots,
     dequantize_rows,
+    query_values,
     attend,
     merge_partials,
     mla_decode_reference,
@@ -68,6 +69,7 @@ __all__ = [
     "ROW_DIM",
     "row_slots",
     "dequantize_rows",
+    "query_values",
     "attend",
     "merge_partials",
     "mla_decode_reference",

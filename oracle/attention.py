@@ -94,8 +94,17 @@ def visible_rows(ctx, seqlen_qo, s, causal) -> int:
     return int(ctx) - int(seqlen_qo) + 1 + int(s) if causal else int(ctx)
 
 
+def query_values(q_rows, q_scale=1.0) -> np.ndarray:
+    """Query rows in float64: bf16 bits (uint16) exactly, or e4m3fn bytes (uint8) times the
+    per-tensor q_scale, the fp8-query x fp8-cache setting of the HK page's fp8_fp8 kernels."""
+    q_rows = np.asarray(q_rows)
+    if q_rows.dtype == np.uint8:
+        return decode_e4m3fn(q_rows) * np.float64(np.float32(q_scale))
+    return bf16_bits_to_f64(q_rows)
+
+
 def mla_decode_reference_one(q_bits, cache_raw, kv_dtype, kv_scale, kv_indptr, kv_page_indices,
-                             context_lens, page_size, softmax_scale, causal, b):
+                             context_lens, page_size, softmax_scale, causal, b, q_scale=1.0):
     """Reference output of one sequence ``b``: (out [S, H, 512], lse [S, H]) in float64."""
     q_bits = np.asarray(q_bits)
     S, H = q_bits.shape[1], q_bits.shape[2]
@@ -107,16 +116,17 @@ def mla_decode_reference_one(q_bits, cache_raw, kv_dtype, kv_scale, kv_indptr, k
     lse = np.zeros((S, H), np.float64)
     for s in range(S):
         n = visible_rows(ctx, S, s, causal)
-        q = bf16_bits_to_f64(q_bits[b, s])  # [H, 576]
+        q = query_values(q_bits[b, s], q_scale)  # [H, 576]
         out[s], lse[s] = attend(q, keys[:n], values[:n], softmax_scale)
     return out, lse
 
 
 def mla_decode_reference(q_bits, cache_raw, kv_dtype, kv_scale, kv_indptr, kv_page_indices,
-                         context_lens, page_size, softmax_scale, causal, batches=None):
+                         context_lens, page_size, softmax_scale, causal, batches=None, q_scale=1.0):
     """Reference MLA decode over the whole batch (or the listed ``batches``).
 
-    q_bits [B, S, H, 576] uint16 (bf16 bits); cache_raw [num_slots, 576] uint16 (bf16)
+    q_bits [B, S, H, 576] uint16 (bf16 bits), or uint8 (fp8 e4m3fn bytes, each times q_scale);
+    cache_raw [num_slots, 576] uint16 (bf16)
     or uint8 (fp8 e4m3fn); kv_indptr [B+1], kv_page_indices, context_lens [B] int.
     Returns (out [B, S, H, 512], lse [B, S, H]) float64; rows of batches not listed
     are left NaN.
@@ -130,5 +140,5 @@ def mla_decode_reference(q_bits, cache_raw, kv_dtype, kv_scale, kv_indptr, kv_pa
     for b in (range(B) if batches is None else batches):
         out[b], lse[b] = mla_decode_reference_one(q_bits, cache_raw, kv_dtype, kv_scale, kv_indptr,
                                                   kv_page_indices, context_lens, page_size,
-                                                  softmax_scale, causal, b)
+                                                  softmax_scale, causal, b, q_scale)
     return out, lse

@@ -62,7 +62,10 @@ def brute_decode(case, use_mpmath=False):
         for s in range(S):
             n = ctx - S + 1 + s if case.causal else ctx
             for h in range(H):
-                q = [num(bf16_value(x)) for x in case.q_bits[b, s, h]]
+                if getattr(case, "q_dtype", "bf16") == "fp8_e4m3fn":
+                    q = [num(e4m3fn_value(x)) * num(case.q_scale) for x in case.q_bits[b, s, h]]
+                else:
+                    q = [num(bf16_value(x)) for x in case.q_bits[b, s, h]]
                 z = [scale * fsum([q[d] * rows[r][d] for d in range(576)]) for r in range(n)]
                 mu = max(z)
                 w = [exp(zr - mu) for zr in z]

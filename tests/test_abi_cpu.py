@@ -94,6 +94,16 @@ def test_host_plan_matches_reference_planner_bit_exactly(shape, force):
     assert mla.workspace_size(p, mla.make_options(force_chunk=force), 256) == plan.ws_bytes
 
 
+def test_fp8_query_params_plan_like_bf16_query():
+    # the query type changes no part of the plan (grid, chunking, workspace)
+    for shape in SHAPES:
+        B, S, H, L = shape
+        a = mla.plan_to_dict(mla.plan_host(params(batch=B, seqlen_qo=S, num_heads=H, max_context_len=L), None, 256))
+        b = mla.plan_to_dict(mla.plan_host(params(batch=B, seqlen_qo=S, num_heads=H, max_context_len=L,
+                                                  q_dtype="fp8_e4m3fn", q_scale=0.02), None, 256))
+        assert a == b
+
+
 def test_non_default_options_follow_the_rule():
     o = mla.make_options(wg_per_cu=[1, 1, 1, 3], chunk_min=[64, 64, 64, 64], chunk_max=[128, 128, 128, 512])
     ro = RefOptions(wg_per_cu=[1, 1, 1, 3], chunk_min=[64, 64, 64, 64], chunk_max=[128, 128, 128, 512])
@@ -110,6 +120,9 @@ def test_non_default_options_follow_the_rule():
     (dict(softmax_scale=float("nan")), 1), (dict(softmax_scale=0.0), 1), (dict(kv_scale=0.0), 1),
     (dict(kv_scale=-1.0), 1), (dict(kv_dtype="bf16", kv_scale=0.5), 1), (dict(num_slots=0), 1),
     (dict(num_slots=4097), 1), (dict(batch=70000), 2), (dict(seqlen_qo=4, max_context_len=3), 1),
+    (dict(q_dtype=2), 1), (dict(q_dtype="fp8_e4m3fn", q_scale=0.0), 1),
+    (dict(q_dtype="fp8_e4m3fn", q_scale=float("inf")), 1), (dict(q_scale=0.5), 1),
+    (dict(q_dtype="fp8_e4m3fn", q_scale=0.5, kv_dtype="bf16", kv_scale=1.0), 2),
 ])
 def test_invalid_params_are_rejected_before_device_work(bad, code):
     p = params(**bad)

@@ -155,10 +155,10 @@ def test_status_too_few_pages_and_bad_slot():
 
 def test_status_ctx_too_long_and_rows_out_of_range():
     c = make_kvb_case(batch=2, num_heads=3, ctx=[300, 100], page_size=1, kv_dtype="bf16", seed=11)
-    k, v, status = run(c, max_context_len=200)  # 2 chunks of 128: rows 256.. of sequence 0 not written
+    k, v, status = run(c, max_context_len=200)  # rows 200.. of sequence 0 are not written
     assert status == 8
-    compare(c, k, v, rows=[(0, r) for r in range(256)] + [(1, r) for r in range(100)], label="ctx too long")
-    assert untouched(k, slice(256, 300)) and untouched(v, slice(256, 300))
+    compare(c, k, v, rows=[(0, r) for r in range(200)] + [(1, r) for r in range(100)], label="ctx too long")
+    assert untouched(k, slice(200, 300)) and untouched(v, slice(200, 300))
     cu = c.cu_ctx.copy()
     k, v, status = run(c, cu_ctx=cu, num_out_rows=350)  # sequence 1 (rows 300..399) does not fit
     assert status == 4

@@ -37,7 +37,8 @@ def upload(case):
         kv_page_indices=case.kv_page_indices, context_lens=case.context_lens, batch=case.batch,
         seqlen_qo=case.seqlen_qo, num_heads=case.num_heads, page_size=case.page_size,
         max_context_len=case.max_context_len, causal=case.causal, kv_dtype=case.kv_dtype,
-        softmax_scale=case.softmax_scale, kv_scale=case.kv_scale, num_slots=case.num_slots)
+        softmax_scale=case.softmax_scale, kv_scale=case.kv_scale, num_slots=case.num_slots,
+        q_dtype=case.q_dtype, q_scale=case.q_scale)
 
 
 def run(case, options=None, inputs=None):
@@ -52,7 +53,7 @@ def run(case, options=None, inputs=None):
 def reference(case, batches=None):
     return oracle.mla_decode_reference(case.q_bits, case.cache_raw, case.kv_dtype, case.kv_scale, case.kv_indptr,
                                        case.kv_page_indices, case.context_lens, case.page_size,
-                                       case.softmax_scale, case.causal, batches=batches)
+                                       case.softmax_scale, case.causal, batches=batches, q_scale=case.q_scale)
 
 
 def assert_close(case, out, lse, batches=None, label=""):
@@ -130,6 +131,24 @@ def test_boundary_grid(kv_dtype, S, H, causal, P):
         dec, out, lse = run(case, options(force_chunk=force))
         check_plan_arrays(case, dec)
         assert_close(case, out, lse, label=f"grid force={force}")
+
+
+# fp8 query x fp8 cache: every tile class, page size and causal shape of the grid above
+GRID_Q8 = [(S, H, causal, P) for (kv, S, H, causal, P) in GRID if kv == "fp8_e4m3fn"]
+
+
+@pytest.mark.parametrize("S,H,causal,P", GRID_Q8)
+def test_boundary_grid_fp8_query(S, H, causal, P):
+    C = 128
+    ctx = [max(S, c) for c in (1, 63, 64, 65, C - 1, C, C + 1, 2 * C + 1)]
+    seed = 3000 + GRID_Q8.index((S, H, causal, P))
+    case = make_case(batch=len(ctx), seqlen_qo=S, num_heads=H, ctx=ctx, page_size=P, kv_dtype="fp8_e4m3fn",
+                     causal=causal, seed=seed, pool_pages=sum(-(-c // P) for c in ctx) + 3, q_dtype="fp8_e4m3fn")
+    assert case.q_bits.dtype == np.uint8
+    for force in (0, C):
+        dec, out, lse = run(case, options(force_chunk=force))
+        check_plan_arrays(case, dec)
+        assert_close(case, out, lse, label=f"fp8 query grid force={force}")
 
 
 # merge paths: at most 8 chunks -> one wave per row; more -> column blocks of 16, 128 or 512
@@ -232,6 +251,10 @@ def test_dense_b64_h128_ctx8192_bf16_sampled():
 
 def test_dense_b64_h128_ctx8192_fp8_sampled():
     _sampled("dense_b64_h128_ctx8192_fp8", lambda c: [0, 17, 63])
+
+
+def test_dense_b64_h128_ctx8192_fp8q_sampled():
+    _sampled("dense_b64_h128_ctx8192_fp8q", lambda c: [0, 23, 63])
 
 
 def test_ragged_b256_h128_fp8_p64_sampled():
