@@ -58,30 +58,46 @@ def algorithmic_counts(case):
 # The sources that make up the decode path (planner, decode and merge kernels, their launch code);
 # the epilogue and the cached-prefix expansion live in files of their own and are not part of it.
 DECODE_SOURCES = ("mla_api.cpp", "mla_internal.h", "mla_kernels.hip", "mla_plan.cpp")
+KVB_SOURCES = ("mla_internal.h", "mla_kv_b_proj.hip")
 
 
-def kernel_source_digest():
-    """First 16 hex digits of the sha256 over the decode path's C/HIP sources."""
+def source_digest(names=DECODE_SOURCES):
+    """First 16 hex digits of the sha256 over the named C/HIP sources of the library."""
     import hashlib
     h = hashlib.sha256()
-    for path in [os.path.join(CSRC, n) for n in DECODE_SOURCES]:
+    for path in [os.path.join(CSRC, n) for n in names]:
         h.update(os.path.basename(path).encode())
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload):
-    """HBM bytes per decode launch from the committed counter summary, if it matches these sources."""
+def kernel_source_digest():
+    """The decode path's source digest."""
+    return source_digest(DECODE_SOURCES)
+
+
+def recorded_fields(name, digest):
+    """The "- key: value" fields of a committed profile summary, if it was taken at these sources."""
     import re
-    path = os.path.join(PROFILES, f"mla_decode_kernel_{workload}_hbm_traffic.md")
+    path = os.path.join(PROFILES, name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         fields = dict(re.findall(r"^- (\w+): (\S+)\s*$", f.read(), flags=re.M))
-    if fields.get("kernel_source_sha256_16") != kernel_source_digest():
-        return None
-    return float(fields["hbm_bytes_per_launch"])
+    return fields if fields.get("kernel_source_sha256_16") == digest else None
+
+
+def recorded_traffic(workload):
+    """HBM bytes per decode launch from the committed counter summary, if it matches these sources."""
+    f = recorded_fields(f"mla_decode_kernel_{workload}_hbm_traffic.md", kernel_source_digest())
+    return None if f is None else float(f["hbm_bytes_per_launch"])
+
+
+def recorded_mfma_busy(kernel, workload, digest):
+    """MFMA-busy percentage (rocprofv3 MfmaUtil) from the committed counter summary, if current."""
+    f = recorded_fields(f"{kernel}_{workload}_mfma_lds.md", digest)
+    return None if f is None else float(f["mfma_busy_pct"])
 
 
 def copy_probe(nbytes=1 << 30, reps=3):
@@ -249,8 +265,13 @@ def kvb_bench(args):
                 "frac": tf / MFMA_BF16_PEAK_TFLOPS}
     else:
         roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}
-    roof.update({"traffic": None, "kernel": "mla_kv_b_proj_kernel", "alg_bytes": nbytes, "alg_flops": flops,
-                 "hbm_gbs": gbs, "note": "event pair around one launch; includes the launch gap"})
+    kd = source_digest(KVB_SOURCES)
+    tf_fields = recorded_fields(f"mla_kv_b_proj_kernel_{args.workload}_hbm_traffic.md", kd)
+    traffic = None if tf_fields is None else float(tf_fields["hbm_bytes_per_launch"]) / (us * 1e-6) / 1e9
+    roof.update({"traffic": traffic, "kernel": "mla_kv_b_proj_kernel", "alg_bytes": nbytes, "alg_flops": flops,
+                 "hbm_gbs": gbs, "kernel_source_sha256_16": kd,
+                 "mfma_busy_pct_counter": recorded_mfma_busy("mla_kv_b_proj_kernel", args.workload, kd),
+                 "note": "event pair around one launch; includes the launch gap"})
     cpu = None
     if not args.no_cpu_baseline:
         t0, done = time.perf_counter(), 0
@@ -399,6 +420,7 @@ def main():
     roof["traffic"] = None if traffic_bytes is None else traffic_bytes / dec_s / 1e9
     roof["traffic_bytes_per_launch"] = traffic_bytes
     roof["kernel_source_sha256_16"] = kernel_source_digest()
+    roof["mfma_busy_pct_counter"] = recorded_mfma_busy("mla_decode_kernel", args.workload, kernel_source_digest())
     roof["kernel"] = "mla_decode_kernel"
     roof["kernel_avg_us"] = float(np.mean(dec_ms) * 1e3)
     roof["alg_bytes"] = nbytes
