@@ -151,6 +151,31 @@ def test_boundary_grid_fp8_query(S, H, causal, P):
         assert_close(case, out, lse, label=f"fp8 query grid force={force}")
 
 
+# shapes the grid does not reach: the largest seqlen_qo (8), one head, 256 heads (two head
+# groups of 128), odd page sizes, a causal context of exactly S rows, lengths just past a chunk
+EDGE = [  # (S, H, causal, P, ctx list)
+    (8, 16, True, 3, [8, 9, 200, 1000]),
+    (8, 1, True, 5, [8, 77, 640]),
+    (1, 1, False, 1, [1, 2, 129, 700]),
+    (1, 256, False, 16, [1, 65, 300]),
+    (5, 24, True, 2, [5, 6, 127, 513]),
+    (2, 200, True, 7, [2, 3, 64, 450]),
+]
+
+
+@pytest.mark.parametrize("q_dtype,kv_dtype", [("bf16", "bf16"), ("bf16", "fp8_e4m3fn"), ("fp8_e4m3fn", "fp8_e4m3fn")])
+@pytest.mark.parametrize("S,H,causal,P,ctx", EDGE)
+def test_edge_shapes(q_dtype, kv_dtype, S, H, causal, P, ctx):
+    seed = 5000 + EDGE.index((S, H, causal, P, ctx)) * 3 + ["bf16", "fp8_e4m3fn"].index(kv_dtype) + \
+        (2 if q_dtype != "bf16" else 0)
+    case = make_case(batch=len(ctx), seqlen_qo=S, num_heads=H, ctx=ctx, page_size=P, kv_dtype=kv_dtype,
+                     causal=causal, seed=seed, pool_pages=sum(-(-c // P) for c in ctx) + 2, q_dtype=q_dtype)
+    for force in (0, 64):
+        dec, out, lse = run(case, options(force_chunk=force))
+        check_plan_arrays(case, dec)
+        assert_close(case, out, lse, label=f"edge S={S} H={H} P={P} force={force}")
+
+
 # merge paths: at most 8 chunks -> one wave per row; more -> column blocks of 16, 128 or 512
 # (by how many rows the batch has). Each case forces 64-row chunks so the merge sees many partials.
 @pytest.mark.parametrize("batch,heads,ctx,expect_many", [
