@@ -59,6 +59,7 @@ def algorithmic_counts(case):
 # the epilogue and the cached-prefix expansion live in files of their own and are not part of it.
 DECODE_SOURCES = ("mla_api.cpp", "mla_internal.h", "mla_kernels.hip", "mla_plan.cpp")
 KVB_SOURCES = ("mla_internal.h", "mla_kv_b_proj.hip")
+INSERT_SOURCES = ("mla_internal.h", "mla_insert.hip")
 
 
 def source_digest(names=DECODE_SOURCES):
@@ -181,6 +182,8 @@ def insert_bench(args):
     nbytes = 2 * T * H * 576 * 2 + T * 576 * 2 + T * (256 + 4 + 8) + written * 576 * e
     us = float(np.mean(ms) * 1e3)
     gbs = nbytes / (us * 1e-6) / 1e9
+    tf = recorded_fields(f"mla_insert_kernel_{args.workload}_hbm_traffic.md", source_digest(INSERT_SOURCES))
+    insert_traffic = None if tf is None else float(tf["hbm_bytes_per_launch"]) / (us * 1e-6) / 1e9
     cpu = None
     if not args.no_cpu_baseline:
         t0, n = time.perf_counter(), 0
@@ -200,7 +203,8 @@ def insert_bench(args):
         "call_us_p10_p50_p90": [float(np.percentile(ms, x) * 1e3) for x in (10, 50, 90)],
         "flush_between_steps": flush is not None,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "mla_insert_kernel",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": insert_traffic, "kernel": "mla_insert_kernel",
+                     "kernel_source_sha256_16": source_digest(INSERT_SOURCES),
                      "alg_bytes": nbytes, "note": "event pair around one launch; includes the launch gap"},
         "cpu_baseline": cpu,
     }), flush=True)
