@@ -260,39 +260,37 @@ def test_short_page_list_and_bad_page_ids_are_flagged_not_read():
     assert_close(case2, out, lse, batches=[0], label="short page list next door")
 
 
-# ------------------------------------------------------------------ full-size workloads, sampled outputs
+# ------------------------------------------------------------------ full-size workloads, every sequence
+# The oracle computes each sequence exactly (numpy fp64 on the host cores): every output row of
+# every benchmark workload is compared, not a sample.
 
-def _sampled(name, sample):
+def _full(name):
     case = make_case(**WORKLOADS[name])
     dec, out, lse = run(case)
     check_plan_arrays(case, dec)
-    batches = sorted(set(sample(case)))
-    assert_close(case, out, lse, batches=batches, label=name)
+    assert_close(case, out, lse, label=name)
 
 
-def test_dense_b64_h128_ctx8192_bf16_sampled():
-    _sampled("dense_b64_h128_ctx8192_bf16", lambda c: [0, 1, 31, 62, 63])
+def test_dense_b64_h128_ctx8192_bf16_full():
+    _full("dense_b64_h128_ctx8192_bf16")
 
 
-def test_dense_b64_h128_ctx8192_fp8_sampled():
-    _sampled("dense_b64_h128_ctx8192_fp8", lambda c: [0, 17, 63])
+def test_dense_b64_h128_ctx8192_fp8_full():
+    _full("dense_b64_h128_ctx8192_fp8")
 
 
-def test_dense_b64_h128_ctx8192_fp8q_sampled():
-    _sampled("dense_b64_h128_ctx8192_fp8q", lambda c: [0, 23, 63])
+def test_dense_b64_h128_ctx8192_fp8q_full():
+    _full("dense_b64_h128_ctx8192_fp8q")
 
 
-def test_ragged_b256_h128_fp8_p64_sampled():
-    def pick(c):
-        order = np.argsort(c.context_lens)
-        return [int(order[0]), int(order[1]), int(order[128]), int(order[-2]), int(order[-1]), 0, 255]
-    _sampled("ragged_b256_h128_fp8_p64", pick)
+def test_ragged_b256_h128_fp8_p64_full():
+    _full("ragged_b256_h128_fp8_p64")
 
 
 @pytest.mark.parametrize("b", [1, 2, 3, 4, 5])
 def test_longctx_h12_ctx109440_fp8(b):
-    _sampled(f"longctx_b{b}_h12_ctx109440_fp8", lambda c: range(c.batch))
+    _full(f"longctx_b{b}_h12_ctx109440_fp8")
 
 
-def test_causal_mtp4_b128_h16_ctx5200_fp8_p16_sampled():
-    _sampled("causal_mtp4_b128_h16_ctx5200_fp8_p16", lambda c: [0, 1, 64, 126, 127])
+def test_causal_mtp4_b128_h16_ctx5200_fp8_p16_full():
+    _full("causal_mtp4_b128_h16_ctx5200_fp8_p16")
