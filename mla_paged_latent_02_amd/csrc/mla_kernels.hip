@@ -461,17 +461,24 @@ struct BlockGather {
       }
     }
   }
-  // prologue: blocks 0 .. NS-2 in flight
-  __device__ __forceinline__ void start() {
+  // prologue, first half: the page ids of blocks 0 .. NS-2 (issued before the
+  // query loads, so both round trips overlap)
+  __device__ __forceinline__ void prefetch_ids() {
     if constexpr (kVecPages) {
       fetch_v(0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NS - 1; ++j) pid_copy(j);
+    }
+  }
+  // prologue, second half: blocks 0 .. NS-2 in flight
+  __device__ __forceinline__ void start() {
+    if constexpr (kVecPages) {
       issue(0);
       if (1 < nblk) fetch_v(1);
     } else {
-      // ids of blocks 0 .. NS-2, then iterations -(NS-1) .. -1 in loop order (id copy of block
-      // i + 2NS - 2, gather of block i + NS - 1), so that the loop's wait counts hold from block 0
-#pragma unroll
-      for (int j = 0; j < NS - 1; ++j) pid_copy(j);
+      // then iterations -(NS-1) .. -1 in loop order (id copy of block i + 2NS - 2,
+      // gather of block i + NS - 1), so that the loop's wait counts hold from block 0
       wait_vmcnt<0>();
 #pragma unroll
       for (int i = -(NS - 1); i < 0; ++i) {
@@ -634,24 +641,39 @@ void mla_decode_kernel(DecodeArgs a) {
   const int i16 = lane & 15;  // MFMA column: head row within the wave's 16-row tile
   const int g4 = lane >> 4;   // MFMA k-group
 
-  // ---- work item: workgroup x runs item x / G of the planner's list for head group x % G
+  // ---- work item: workgroup x runs item x / G of the planner's list for head group x % G.
+  // Every load before the first cache row is a cold round trip, so they go in
+  // three dependent batches: the list count with the item (the list holds
+  // grid / G entries, so an item past the count is still in bounds), then the
+  // sequence's fields, then its first page ids together with the query. The
+  // empty asm statements keep the compiler from spreading a batch over
+  // several waits.
   const int item = (int)(blockIdx.x / (unsigned)a.num_groups);
   const int grp = (int)blockIdx.x - item * a.num_groups;
-  if (item >= (int)a.status[1]) return;  // past the list
+  const int count = (int)a.status[1];
   const int b = a.work[2 * item];
   const int chunk = a.work[2 * item + 1];
-  if (chunk < 0) {  // invalid sequence: NaN rows
+  asm volatile("" ::"s"(count), "s"(b), "s"(chunk));
+  if (item >= count) return;  // past the list
+  if (chunk < 0) {            // invalid sequence: NaN rows
     fill_invalid_rows(a, b, grp, wave, NW, lane);
     return;
   }
-  const int n_b = a.nchunks[b];
-
   const int ctx = a.context_lens[b];
+  const int page_base = a.kv_indptr[b];
+  const int n_b = a.nchunks[b];
+  const int rec_base = a.partbase[b];
+  asm volatile("" ::"s"(ctx), "s"(page_base), "s"(n_b), "s"(rec_base));
+
   const int c_start = chunk * a.chunk_len;
   const int c_end = min(c_start + a.chunk_len, ctx);
   int vis_end, row_out;
   bool row_ok;
   tile_row(a, b, grp, hw * 16 + i16, ctx, c_end, vis_end, row_out, row_ok);
+  typename Cfg::Gather gather(a, (uint32_t)(uintptr_t)lds, (uint32_t)(uintptr_t)lds + NS * L::kBlockBytes, c_start,
+                              c_end, page_base, wave, lane);
+  const int nblk = gather.nblk;
+  gather.prefetch_ids();  // in flight with the query loads below
 
   // ---- query fragments (B operand of S^T = K Q^T), resident for the whole chunk.
   // bf16 cache: qf[t] holds d = 32t + 8*g4 .. +7 (18 fragments).
@@ -764,10 +786,6 @@ void mla_decode_kernel(DecodeArgs a) {
   f32x4_t o_acc[32];
 #pragma unroll
   for (int nt = 0; nt < 32; ++nt) o_acc[nt] = f32x4_t{0, 0, 0, 0};
-
-  typename Cfg::Gather gather(a, (uint32_t)(uintptr_t)lds, (uint32_t)(uintptr_t)lds + NS * L::kBlockBytes, c_start,
-                              c_end, a.kv_indptr[b], wave, lane);
-  const int nblk = gather.nblk;
 
   // Per-lane LDS offsets that do not change over the loop; each access adds a
   // compile-time immediate.
@@ -993,7 +1011,7 @@ void mla_decode_kernel(DecodeArgs a) {
   const float lse2 = empty ? -__builtin_inff() : m_fin + __log2f(l_tot);
   if (!row_ok) return;
   const int rr = hw * 16 + i16;
-  const int64_t rec = (int64_t)a.partbase[b] + (int64_t)grp * n_b + chunk;
+  const int64_t rec = (int64_t)rec_base + (int64_t)grp * n_b + chunk;
   const int64_t prec_row = rec * a.rows_per_group + rr;
 #pragma unroll
   for (int nt = 0; nt < 32; ++nt)
@@ -1067,11 +1085,13 @@ __global__ __launch_bounds__(256) void mla_combine_rows_kernel(CombineArgs a) {
   const int bg = (int)(r / rows), rr = (int)(r - (int64_t)bg * rows);
   const int b = bg / a.num_groups, grp = bg - b * a.num_groups;
   const int n_b = a.nchunks[b];
+  const int pbase = a.partbase[b];
+  asm volatile("" ::"s"(n_b), "s"(pbase));  // one round trip for both
   if (n_b <= 1) return;
   const int s = rr / a.heads_per_group;
   const int head = grp * a.heads_per_group + rr % a.heads_per_group;
   if (head >= a.num_heads) return;
-  const int64_t rec0 = (int64_t)a.partbase[b] + (int64_t)grp * n_b;
+  const int64_t rec0 = (int64_t)pbase + (int64_t)grp * n_b;
   const int64_t rec_stride = (int64_t)rows * kLatentDim;
   const float* src = a.part_out + (rec0 * rows + rr) * kLatentDim + 4 * lane;
   const float* lse_src = a.part_lse + rec0 * rows + rr;
@@ -1103,6 +1123,8 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
   const int b = blockIdx.z / a.num_groups;
   const int grp = blockIdx.z % a.num_groups;
   const int n_b = a.nchunks[b];
+  const int pbase = a.partbase[b];
+  asm volatile("" ::"s"(n_b), "s"(pbase));  // one round trip for both
   if (n_b <= 1 || rr >= a.rows_per_group) return;
   const int s = rr / a.heads_per_group;
   const int head = grp * a.heads_per_group + rr % a.heads_per_group;
@@ -1110,7 +1132,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
   const int tid = threadIdx.x;
   const int stream = tid / kThreadsPerChunk;
   const int quad = tid % kThreadsPerChunk;
-  const int64_t rec0 = (int64_t)a.partbase[b] + (int64_t)grp * n_b;
+  const int64_t rec0 = (int64_t)pbase + (int64_t)grp * n_b;
   const float* lse_base = a.part_lse + rec0 * a.rows_per_group + rr;
   const float* out_base = a.part_out + (rec0 * a.rows_per_group + rr) * kLatentDim + colblk * CB + quad * 4;
   const int64_t rec_stride = (int64_t)a.rows_per_group * kLatentDim;
