@@ -1230,7 +1230,7 @@ int launch_decode(const DecodeArgs& a, int kv_dtype, bool q_fp8, int tile_class,
     switch (tile_class) {
       case 0: return launch_decode_t<true, 1, 4, 2, 1, 4, 8, 4, true>(a, gx, gy, gz, st);
       case 1: return launch_decode_t<true, 2, 2, 4, 1, 4, 8, 4, true>(a, gx, gy, gz, st);
-      case 2: return launch_decode_t<true, 4, 2, 4, 2, 2, 3, 1, true>(a, gx, gy, gz, st);
+      case 2: return launch_decode_t<true, 4, 1, 4, 2, 3, 3, 1, true>(a, gx, gy, gz, st);
       case 3: return launch_decode_t<true, 8, 1, 8, 2, 3, 3, 1, true>(a, gx, gy, gz, st);
     }
     return (int)hipErrorInvalidValue;
@@ -1240,8 +1240,8 @@ int launch_decode(const DecodeArgs& a, int kv_dtype, bool q_fp8, int tile_class,
                        : launch_decode_t<false, 1, 2, 2, 1, 8, 8, 4>(a, gx, gy, gz, st);
     case 1: return fp8 ? launch_decode_t<true, 2, 2, 4, 1, 4, 8, 4>(a, gx, gy, gz, st)
                        : launch_decode_t<false, 2, 2, 2, 1, 8, 8, 4>(a, gx, gy, gz, st);
-    case 2: return fp8 ? launch_decode_t<true, 4, 2, 4, 2, 2, 3, 1>(a, gx, gy, gz, st)
-                       : launch_decode_t<false, 4, 2, 2, 2, 3, 3, 2>(a, gx, gy, gz, st);
+    case 2: return fp8 ? launch_decode_t<true, 4, 1, 4, 2, 3, 3, 1>(a, gx, gy, gz, st)
+                       : launch_decode_t<false, 4, 1, 2, 2, 4, 3, 1>(a, gx, gy, gz, st);
     case 3: return fp8 ? launch_decode_t<true, 8, 1, 8, 2, 3, 3, 1>(a, gx, gy, gz, st)
                        : launch_decode_t<false, 8, 1, 4, 2, 4, 3, 1>(a, gx, gy, gz, st);
   }

@@ -37,9 +37,10 @@ def test_plan_values_for_the_benchmark_shapes():
     # Hand-derived from the rule with the default options and 256 CUs.
     p = reference_plan(64, 1, 128, 8192, 256)
     assert (p["heads_per_group"], p["num_groups"], p["tile_rows"], p["chunk_len"], p["max_chunks"]) == (128, 1, 128, 2048, 4)
-    # 16 heads x 4 tokens: want = floor(256 / 128) = 2 -> ceil(5200 / 2) = 2600 -> 2624 rows, 2 chunks
+    # 16 heads x 4 tokens, 64-row tiles at two workgroups per CU: want = floor(256 * 2 / 128) = 4
+    # -> ceil(5200 / 4) = 1300 -> 1344 rows, 4 chunks
     p = reference_plan(128, 4, 16, 5200, 256)
-    assert (p["heads_per_group"], p["tile_rows"], p["chunk_len"], p["max_chunks"]) == (16, 64, 2624, 2)
+    assert (p["heads_per_group"], p["tile_rows"], p["chunk_len"], p["max_chunks"]) == (16, 64, 1344, 4)
     # 256 x 128 heads: want = 1 -> ceil(23333 / 1) rounds to 23360 -> capped at chunk_max = 6144, 4 chunks
     p = reference_plan(256, 1, 128, 23333, 256)
     assert (p["chunk_len"], p["max_chunks"]) == (6144, 4)
