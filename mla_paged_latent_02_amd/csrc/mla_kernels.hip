@@ -808,6 +808,13 @@ void mla_decode_kernel(DecodeArgs a) {
 
   gather.start();
   const float sscale = a.score_scale_log2;
+  // Wave priority: two waves share each SIMD, and while one runs its softmax
+  // (and, for an fp8 cache, widens V) the other should keep the matrix pipe
+  // fed, so a wave raises its priority for its MFMA phases. Measured per
+  // configuration: the 128-row fp8 kernel with a bf16 query is fastest with
+  // only QK^T raised (its PV phase carries the V widening), the others with
+  // both phases raised (no effect on the bf16 kernels).
+  constexpr bool kPrioPV = !(FP8 && !QF8 && HW == 8);
 
   for (int blk = 0; blk < nblk; ++blk) {
     gather.wait(blk);
@@ -819,6 +826,7 @@ void mla_decode_kernel(DecodeArgs a) {
     LDS_PTR(uint8_t) tstage = stage + (uint32_t)(L::kTailBase + kw * 32 * L::kTailBytes);
     const int kv0 = c_start + blk * BN + kw * 32;
 
+    __builtin_amdgcn_s_setprio(1);
     // ---- S^T[kv, head] = K Q^T for the wave's 32 rows of the block (two tiles of 16 kv rows).
     // The LDS reads run in a ring of KD units in flight. Each tile's sum over
     // the dims is split over QC accumulators (the tile's m-th MFMA goes to chain
@@ -896,6 +904,7 @@ void mla_decode_kernel(DecodeArgs a) {
       }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     // ---- mask, online softmax
     float alpha;
     bool up;
@@ -906,6 +915,7 @@ void mla_decode_kernel(DecodeArgs a) {
       for (int nt = 0; nt < 32; ++nt) o_acc[nt] *= alpha;
     }
 
+    if constexpr (kPrioPV) __builtin_amdgcn_s_setprio(1);
     // ---- O^T[n, head] += V^T P^T ; V^T fragments by transposed LDS reads.
     // Lane (head, g4) of P^T holds the wave's rows 4g4 + r (r < 4) then
     // 16 + 4g4 + r; the V^T fragment holds the same rows, in the same order,
@@ -946,6 +956,7 @@ void mla_decode_kernel(DecodeArgs a) {
         MLA_STEP_BARRIER();
       }
     }
+    if constexpr (kPrioPV) __builtin_amdgcn_s_setprio(0);
   }
   gather.report(a.status);
 
