@@ -136,7 +136,7 @@ int32_t mla_abi_version(void);
 const char* mla_status_string(mla_status_t status);
 
 /* Fills *out with the default tunables: wg_per_cu {1, 1, 2, 1} (the LDS that
- * each tile class's kernel holds per workgroup), chunk_min {256, 256, 256, 1024},
+ * each tile class's kernel holds per workgroup), chunk_min {256, 256, 256, 128},
  * chunk_max {8192, 8192, 4096, 6144}, force_chunk 0. */
 void mla_plan_options_default(mla_plan_options_t* out);
 

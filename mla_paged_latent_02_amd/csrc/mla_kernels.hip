@@ -1085,8 +1085,22 @@ __device__ __forceinline__ void merge_row(const CombineArgs& a, const float* src
   if (a.lse && lane == 0) a.lse[orow] = total > 0.0f ? (M + __log2f(total)) * kLn2 : -__builtin_inff();
 }
 
-// Split-KV merge when no sequence has more than 8 chunks: one wave per output
-// row, dispatched on the row's chunk count, no LDS.
+// The row's merge for its chunk count n (2 <= n <= N), unrolled for each count.
+template <int N>
+__device__ __forceinline__ void merge_row_upto(int n, const CombineArgs& a, const float* src, int64_t rec_stride,
+                                               const float* lse_src, int64_t orow, int lane) {
+  if (n == N) {
+    merge_row<N>(a, src, rec_stride, lse_src, orow, lane);
+  } else if constexpr (N > 2) {
+    merge_row_upto<N - 1>(n, a, src, rec_stride, lse_src, orow, lane);
+  }
+}
+
+// Split-KV merge when no sequence has more than MAXN chunks: one wave per
+// output row, dispatched on the row's chunk count, no LDS. Two instances
+// (MAXN = 8 and 16) so that the common few-chunk merges keep the register
+// count, and the occupancy, of an 8-chunk body.
+template <int MAXN>
 __global__ __launch_bounds__(256) void mla_combine_rows_kernel(CombineArgs a) {
   const int lane = threadIdx.x & 63;
   const int rows = a.rows_per_group;
@@ -1098,7 +1112,7 @@ __global__ __launch_bounds__(256) void mla_combine_rows_kernel(CombineArgs a) {
   const int n_b = a.nchunks[b];
   const int pbase = a.partbase[b];
   asm volatile("" ::"s"(n_b), "s"(pbase));  // one round trip for both
-  if (n_b <= 1) return;
+  if (n_b <= 1 || n_b > MAXN) return;  // the launcher picks MAXN >= the plan's chunk count
   const int s = rr / a.heads_per_group;
   const int head = grp * a.heads_per_group + rr % a.heads_per_group;
   if (head >= a.num_heads) return;
@@ -1107,16 +1121,7 @@ __global__ __launch_bounds__(256) void mla_combine_rows_kernel(CombineArgs a) {
   const float* src = a.part_out + (rec0 * rows + rr) * kLatentDim + 4 * lane;
   const float* lse_src = a.part_lse + rec0 * rows + rr;
   const int64_t orow = ((int64_t)b * a.seqlen_qo + s) * a.num_heads + head;
-  switch (n_b) {
-    case 2: merge_row<2>(a, src, rec_stride, lse_src, orow, lane); break;
-    case 3: merge_row<3>(a, src, rec_stride, lse_src, orow, lane); break;
-    case 4: merge_row<4>(a, src, rec_stride, lse_src, orow, lane); break;
-    case 5: merge_row<5>(a, src, rec_stride, lse_src, orow, lane); break;
-    case 6: merge_row<6>(a, src, rec_stride, lse_src, orow, lane); break;
-    case 7: merge_row<7>(a, src, rec_stride, lse_src, orow, lane); break;
-    case 8: merge_row<8>(a, src, rec_stride, lse_src, orow, lane); break;
-    default: break;  // the launcher only picks this kernel when max_chunks <= 8
-  }
+  merge_row_upto<MAXN>(n_b, a, src, rec_stride, lse_src, orow, lane);
 }
 
 // Split-KV merge for any chunk count: column blocks of CB, streams of threads
@@ -1259,17 +1264,19 @@ int launch_decode(const DecodeArgs& a, int kv_dtype, bool q_fp8, int tile_class,
   return (int)hipErrorInvalidValue;
 }
 
-constexpr int kCombineRowsMaxChunks = 8;
 
 int launch_combine(const CombineArgs& a, int max_chunks, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const int rows = a.rows_per_group;
   const int gz = a.batch * a.num_groups;
   const int64_t row_count = (int64_t)gz * rows;
-  if (max_chunks <= kCombineRowsMaxChunks) {
+  if (max_chunks <= 16) {
     const int64_t wgs = (row_count + 3) / 4;
     if (wgs > 0x7fffffff) return (int)hipErrorInvalidValue;
-    hipLaunchKernelGGL(mla_combine_rows_kernel, dim3((unsigned)wgs), dim3(256), 0, st, a);
+    if (max_chunks <= 8)
+      hipLaunchKernelGGL(mla_combine_rows_kernel<8>, dim3((unsigned)wgs), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(mla_combine_rows_kernel<16>, dim3((unsigned)wgs), dim3(256), 0, st, a);
     return (int)hipGetLastError();
   }
   // Narrow column blocks when few rows carry long chunk lists.

@@ -164,6 +164,12 @@ WORKLOADS = {
     "dense_b64_h128_ctx8192_fp8q": dict(batch=64, seqlen_qo=1, num_heads=128, ctx=8192, page_size=1,
                                         kv_dtype="fp8_e4m3fn", q_dtype="fp8_e4m3fn", seed=7),
 }
+# small batches of the same 128-head shape, fp8 query x fp8 cache as in the HK page's
+# results table (its batch sweep at ctx 8192)
+for _b, _seed in ((1, 8), (5, 9), (16, 10)):
+    WORKLOADS[f"small_b{_b}_h128_ctx8192_fp8q"] = dict(batch=_b, seqlen_qo=1, num_heads=128, ctx=8192,
+                                                       page_size=1, kv_dtype="fp8_e4m3fn",
+                                                       q_dtype="fp8_e4m3fn", seed=_seed)
 for _b in range(1, 6):
     WORKLOADS[f"longctx_b{_b}_h12_ctx109440_fp8"] = dict(batch=_b, seqlen_qo=1, num_heads=12, ctx=109440,
                                                           page_size=1, kv_dtype="fp8_e4m3fn", seed=40 + _b)

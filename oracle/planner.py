@@ -65,7 +65,7 @@ def _cdiv(a: int, b: int) -> int:
 @dataclass
 class PlanOptions:
     wg_per_cu: List[int] = field(default_factory=lambda: [1, 1, 2, 1])
-    chunk_min: List[int] = field(default_factory=lambda: [256, 256, 256, 1024])
+    chunk_min: List[int] = field(default_factory=lambda: [256, 256, 256, 128])
     chunk_max: List[int] = field(default_factory=lambda: [8192, 8192, 4096, 6144])
     force_chunk: int = 0
 
