@@ -104,6 +104,17 @@ def test_fp8_query_params_plan_like_bf16_query():
         assert a == b
 
 
+def test_default_options_match_the_header_and_the_oracle():
+    # the defaults the header documents, the library's and the oracle planner's agree
+    here = os.path.dirname(os.path.abspath(__file__))
+    text = open(os.path.join(here, "..", "include", "mla_decode.h")).read()
+    o, ro = mla.default_options(), RefOptions()
+    for name in ("wg_per_cu", "chunk_min", "chunk_max"):
+        doc = [int(x) for x in re.search(name + r" \{([\d, ]+)\}", text).group(1).split(",")]
+        assert list(getattr(o, name)) == doc == list(getattr(ro, name)), name
+    assert o.force_chunk == 0 == ro.force_chunk
+
+
 def test_non_default_options_follow_the_rule():
     o = mla.make_options(wg_per_cu=[1, 1, 1, 3], chunk_min=[64, 64, 64, 64], chunk_max=[128, 128, 128, 512])
     ro = RefOptions(wg_per_cu=[1, 1, 1, 3], chunk_min=[64, 64, 64, 64], chunk_max=[128, 128, 128, 512])
