@@ -41,6 +41,11 @@ def test_plan_values_for_the_benchmark_shapes():
     # -> ceil(5200 / 4) = 1300 -> 1344 rows, 4 chunks
     p = reference_plan(128, 4, 16, 5200, 256)
     assert (p["heads_per_group"], p["tile_rows"], p["chunk_len"], p["max_chunks"]) == (16, 64, 1344, 4)
+    # small batches of 128 heads at ctx 8192: b = 1: want = 256 -> 32 -> 64 rows, raised to chunk_min = 128,
+    # 64 chunks; b = 5: want = 51 -> 161 -> 192 rows, 43 chunks; b = 16: want = 16 -> 512 rows, 16 chunks
+    for b, C, n in ((1, 128, 64), (5, 192, 43), (16, 512, 16)):
+        p = reference_plan(b, 1, 128, 8192, 256)
+        assert (p["tile_rows"], p["chunk_len"], p["max_chunks"]) == (128, C, n), b
     # 256 x 128 heads: want = 1 -> ceil(23333 / 1) rounds to 23360 -> capped at chunk_max = 6144, 4 chunks
     p = reference_plan(256, 1, 128, 23333, 256)
     assert (p["chunk_len"], p["max_chunks"]) == (6144, 4)
