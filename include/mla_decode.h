@@ -149,7 +149,8 @@ void mla_plan_options_default(mla_plan_options_t* out);
  * sequence; "HK MLA ..." Summary: rows = heads x query tokens, num_cu clusters):
  *   hpg = min(H, 128/S); G = ceil(H/hpg); TR = smallest of 16/32/64/128 >= hpg*S
  *   C = force_chunk or clamp(roundup(ceil(Lmax / want), 64), chunk_min, chunk_max),
- *       want = max(1, floor(num_cu * wg_per_cu / (B*G)))
+ *       want = max(1, floor(num_cu * min(wg_per_cu, fit) / (B*G))), fit = workgroups per CU that
+ *       the decode kernel of the class and cache type holds: 2 for fp8 64-row tiles, else 1
  *   max_chunks = ceil(Lmax / C), work_capacity = B * max_chunks, grid = (work_capacity * G, 1, 1)
  */
 mla_status_t mla_decode_plan_host(const mla_decode_params_t* params, const mla_plan_options_t* options,

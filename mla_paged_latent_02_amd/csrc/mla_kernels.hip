@@ -1257,7 +1257,7 @@ int launch_decode(const DecodeArgs& a, int kv_dtype, bool q_fp8, int tile_class,
     case 1: return fp8 ? launch_decode_t<true, 2, 2, 4, 1, 4, 8, 4>(a, gx, gy, gz, st)
                        : launch_decode_t<false, 2, 2, 2, 1, 8, 8, 4>(a, gx, gy, gz, st);
     case 2: return fp8 ? launch_decode_t<true, 4, 1, 4, 2, 3, 3, 1>(a, gx, gy, gz, st)
-                       : launch_decode_t<false, 4, 1, 2, 2, 4, 3, 1>(a, gx, gy, gz, st);
+                       : launch_decode_t<false, 4, 2, 2, 2, 3, 3, 2>(a, gx, gy, gz, st);
     case 3: return fp8 ? launch_decode_t<true, 8, 1, 8, 2, 3, 3, 1>(a, gx, gy, gz, st)
                        : launch_decode_t<false, 8, 1, 4, 2, 4, 3, 1>(a, gx, gy, gz, st);
   }

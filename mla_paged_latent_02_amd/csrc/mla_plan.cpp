@@ -114,7 +114,12 @@ mla_status_t mla_decode_plan_host(const mla_decode_params_t* params, const mla_p
   if (opt.force_chunk) {
     C = opt.force_chunk;
   } else {
-    int64_t want = int64_t(num_cu) * opt.wg_per_cu[cls] / (B * G);
+    // the target is capped at the workgroups the class's decode kernel fits per CU
+    // (its LDS footprint): only the fp8 64-row kernel holds two
+    static const int32_t kFit[2][4] = {{1, 1, 1, 1}, {1, 1, 2, 1}};  // [bf16, fp8][class]
+    const int32_t fit = kFit[p.kv_dtype == MLA_KV_FP8_E4M3FN ? 1 : 0][cls];
+    const int64_t wg = opt.wg_per_cu[cls] < fit ? opt.wg_per_cu[cls] : fit;
+    int64_t want = int64_t(num_cu) * wg / (B * G);
     if (want < 1) want = 1;
     C = cdiv(cdiv(L, want), mla::kBlockRows) * mla::kBlockRows;
     if (C < opt.chunk_min[cls]) C = opt.chunk_min[cls];

@@ -24,7 +24,8 @@ The rule (all integer arithmetic):
     TR   = 16 | 32 | 64 | 128          smallest of these >= rows; class = log2(TR/16)
     C    = force_chunk if set, else
            clamp(roundup(ceil(Lmax / want), 64), chunk_min[cls], chunk_max[cls])
-           with want = max(1, floor(num_cu * wg_per_cu[cls] / (B * G)))
+           with want = max(1, floor(num_cu * min(wg_per_cu[cls], fit[kv_dtype][cls]) / (B * G)))
+           (fit: workgroups the decode kernel of that cache type and class holds per CU)
     max_chunks = ceil(Lmax / C)
     work_capacity = B * max_chunks     decode grid = (work_capacity * G, 1, 1)
 
@@ -62,6 +63,11 @@ def _cdiv(a: int, b: int) -> int:
     return -(-a // b)
 
 
+# workgroups per CU that the decode kernel of each cache type and tile class fits
+# (its LDS footprint); the target wg_per_cu is capped at it
+KERNEL_WG_PER_CU = {"bf16": [1, 1, 1, 1], "fp8_e4m3fn": [1, 1, 2, 1]}
+
+
 @dataclass
 class PlanOptions:
     wg_per_cu: List[int] = field(default_factory=lambda: [1, 1, 2, 1])
@@ -70,8 +76,9 @@ class PlanOptions:
     force_chunk: int = 0
 
 
-def reference_plan(batch, seqlen_qo, num_heads, max_context_len, num_cu, options=None):
-    """Plan fields for one call shape. Returns a dict; see the module docstring."""
+def reference_plan(batch, seqlen_qo, num_heads, max_context_len, num_cu, options=None, *, kv_dtype):
+    """Plan fields for one call shape and cache type ("bf16" or "fp8_e4m3fn"). Returns a dict;
+    see the module docstring."""
     o = options or PlanOptions()
     B, S, H, L = int(batch), int(seqlen_qo), int(num_heads), int(max_context_len)
     hpg = min(H, MAX_TILE_ROWS // S)
@@ -82,7 +89,8 @@ def reference_plan(batch, seqlen_qo, num_heads, max_context_len, num_cu, options
     if o.force_chunk:
         C = int(o.force_chunk)
     else:
-        want = max(1, (num_cu * o.wg_per_cu[cls]) // (B * G))
+        wg = min(o.wg_per_cu[cls], KERNEL_WG_PER_CU[kv_dtype][cls])
+        want = max(1, (num_cu * wg) // (B * G))
         C = _cdiv(_cdiv(L, want), BLOCK_ROWS) * BLOCK_ROWS
         C = min(max(C, o.chunk_min[cls]), o.chunk_max[cls])
     max_chunks = _cdiv(L, C)

@@ -74,11 +74,13 @@ SHAPES = [(2, 1, 16, 100), (64, 1, 128, 8192), (256, 1, 128, 23333), (1, 1, 12, 
 
 @pytest.mark.parametrize("shape", SHAPES)
 @pytest.mark.parametrize("force", [0, 64, 320])
-def test_host_plan_matches_reference_planner_bit_exactly(shape, force):
+@pytest.mark.parametrize("dt", ["bf16", "fp8_e4m3fn"])
+def test_host_plan_matches_reference_planner_bit_exactly(shape, force, dt):
     B, S, H, L = shape
-    p = params(batch=B, seqlen_qo=S, num_heads=H, max_context_len=L)
+    p = params(batch=B, seqlen_qo=S, num_heads=H, max_context_len=L, kv_dtype=dt,
+               kv_scale=1.0 if dt == "bf16" else 0.01)
     plan = mla.plan_host(p, mla.make_options(force_chunk=force), num_cu=256)
-    ref = reference_plan(B, S, H, L, 256, RefOptions(force_chunk=force))
+    ref = reference_plan(B, S, H, L, 256, RefOptions(force_chunk=force), kv_dtype=dt)
     got = mla.plan_to_dict(plan)
     assert got == {k: ref[k] for k in got}
     assert plan.magic == 0x4D4C4131
@@ -121,7 +123,7 @@ def test_non_default_options_follow_the_rule():
     for shape in SHAPES:
         B, S, H, L = shape
         got = mla.plan_to_dict(mla.plan_host(params(batch=B, seqlen_qo=S, num_heads=H, max_context_len=L), o, 304))
-        ref = reference_plan(B, S, H, L, 304, ro)
+        ref = reference_plan(B, S, H, L, 304, ro, kv_dtype="fp8_e4m3fn")
         assert got == {k: ref[k] for k in got}
 
 

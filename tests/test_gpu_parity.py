@@ -73,7 +73,7 @@ def check_plan_arrays(case, dec):
     import mla_paged_latent_02_amd as mla
     n, base, status = mla.read_plan_arrays(dec.plan, dec.workspace)
     ref = oracle.reference_plan(case.batch, case.seqlen_qo, case.num_heads, case.max_context_len,
-                                dec.plan.num_cu, _ref_options(dec.plan))
+                                dec.plan.num_cu, _ref_options(dec.plan), kv_dtype=case.kv_dtype)
     assert mla.plan_to_dict(dec.plan) == {k: ref[k] for k in mla.plan_to_dict(dec.plan)}
     rn, rbase, rstatus = oracle.device_plan_arrays(ref, case.seqlen_qo, case.max_context_len, case.page_size,
                                                    case.context_lens, case.kv_indptr)

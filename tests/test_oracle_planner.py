@@ -22,7 +22,7 @@ SHAPES = [
 @pytest.mark.parametrize("shape", SHAPES)
 def test_plan_structure(shape):
     B, S, H, L = shape
-    p = reference_plan(B, S, H, L, num_cu=256)
+    p = reference_plan(B, S, H, L, num_cu=256, kv_dtype="bf16")
     hpg, G, rows, TR, C = p["heads_per_group"], p["num_groups"], p["rows_per_group"], p["tile_rows"], p["chunk_len"]
     assert 1 <= hpg <= H and hpg * S <= 128 and rows == hpg * S
     assert G * hpg >= H and (G - 1) * hpg < H  # groups cover every head, no empty group
@@ -35,29 +35,33 @@ def test_plan_structure(shape):
 
 def test_plan_values_for_the_benchmark_shapes():
     # Hand-derived from the rule with the default options and 256 CUs.
-    p = reference_plan(64, 1, 128, 8192, 256)
+    p = reference_plan(64, 1, 128, 8192, 256, kv_dtype="bf16")
     assert (p["heads_per_group"], p["num_groups"], p["tile_rows"], p["chunk_len"], p["max_chunks"]) == (128, 1, 128, 2048, 4)
     # 16 heads x 4 tokens, 64-row tiles at two workgroups per CU: want = floor(256 * 2 / 128) = 4
     # -> ceil(5200 / 4) = 1300 -> 1344 rows, 4 chunks
-    p = reference_plan(128, 4, 16, 5200, 256)
+    p = reference_plan(128, 4, 16, 5200, 256, kv_dtype="fp8_e4m3fn")
     assert (p["heads_per_group"], p["tile_rows"], p["chunk_len"], p["max_chunks"]) == (16, 64, 1344, 4)
+    # the same shape with a bf16 cache: its 64-row kernel fits one workgroup per CU, so the target of 2
+    # is capped at 1: want = 2 -> 2600 -> 2624 rows, 2 chunks
+    p = reference_plan(128, 4, 16, 5200, 256, kv_dtype="bf16")
+    assert (p["chunk_len"], p["max_chunks"]) == (2624, 2)
     # small batches of 128 heads at ctx 8192: b = 1: want = 256 -> 32 -> 64 rows, raised to chunk_min = 128,
     # 64 chunks; b = 5: want = 51 -> 161 -> 192 rows, 43 chunks; b = 16: want = 16 -> 512 rows, 16 chunks
     for b, C, n in ((1, 128, 64), (5, 192, 43), (16, 512, 16)):
-        p = reference_plan(b, 1, 128, 8192, 256)
+        p = reference_plan(b, 1, 128, 8192, 256, kv_dtype="fp8_e4m3fn")
         assert (p["tile_rows"], p["chunk_len"], p["max_chunks"]) == (128, C, n), b
     # 256 x 128 heads: want = 1 -> ceil(23333 / 1) rounds to 23360 -> capped at chunk_max = 6144, 4 chunks
-    p = reference_plan(256, 1, 128, 23333, 256)
+    p = reference_plan(256, 1, 128, 23333, 256, kv_dtype="fp8_e4m3fn")
     assert (p["chunk_len"], p["max_chunks"]) == (6144, 4)
     # 12 heads, one sequence: want = 256 -> ceil(109440 / 256) = 428 -> 448 rows, 245 chunks
-    p = reference_plan(1, 1, 12, 109440, 256)
+    p = reference_plan(1, 1, 12, 109440, 256, kv_dtype="fp8_e4m3fn")
     assert (p["tile_rows"], p["chunk_len"], p["max_chunks"]) == (16, 448, 245)
     # five sequences: want = floor(256 / 5) = 51 -> 2146 -> 2176 rows, 51 chunks, 255 workgroups
     # (a ceiling would give 52 -> 2112 rows -> 52 chunks, 260 workgroups on 256 CUs)
-    p = reference_plan(5, 1, 12, 109440, 256)
+    p = reference_plan(5, 1, 12, 109440, 256, kv_dtype="fp8_e4m3fn")
     assert (p["chunk_len"], p["max_chunks"]) == (2176, 51)
     assert 5 * p["max_chunks"] <= 256
-    p = reference_plan(2, 1, 16, 100, 256, PlanOptions(force_chunk=64))
+    p = reference_plan(2, 1, 16, 100, 256, PlanOptions(force_chunk=64), kv_dtype="bf16")
     assert (p["chunk_len"], p["max_chunks"]) == (64, 2)
 
 
@@ -68,7 +72,7 @@ def test_device_arrays_tile_every_context_exactly(seed):
     lens = rng.integers(S, 3000, size=B)
     L = int(lens.max())
     indptr = np.concatenate([[0], np.cumsum(_cdiv(lens, P))])
-    p = reference_plan(B, S, H, L, 256, PlanOptions(force_chunk=int(rng.choice([0, 64, 192]))))
+    p = reference_plan(B, S, H, L, 256, PlanOptions(force_chunk=int(rng.choice([0, 64, 192]))), kv_dtype="bf16")
     n, base, status = device_plan_arrays(p, S, L, P, lens, indptr)
     assert status == 0
     C, G = p["chunk_len"], p["num_groups"]
@@ -87,7 +91,7 @@ def test_device_arrays_tile_every_context_exactly(seed):
 
 
 def test_device_status_bits():
-    p = reference_plan(4, 2, 8, 100, 256)
+    p = reference_plan(4, 2, 8, 100, 256, kv_dtype="bf16")
     lens = [1, 101, 50, 50]
     indptr = [0, 1, 102, 103, 153]  # seq 2 has 1 page of size 1 for 50 rows
     n, base, status = device_plan_arrays(p, 2, 100, 1, lens, indptr)
@@ -99,7 +103,7 @@ def test_work_list_hand_example():
     # C = 64: ctx 200 -> chunks of 64, 64, 64, 8 (last: class 16*8//64 = 2);
     # ctx 64 -> one full chunk; ctx 100 -> 64 + 36 (class 9); ctx 0 < S -> invalid;
     # ctx 120 -> 64 + 56 (class 14)
-    plan = reference_plan(5, 1, 16, 200, 256, PlanOptions(force_chunk=64))
+    plan = reference_plan(5, 1, 16, 200, 256, PlanOptions(force_chunk=64), kv_dtype="bf16")
     lens = [200, 64, 100, 0, 120]
     n, _, status = device_plan_arrays(plan, 1, 200, 1, lens, [0, 200, 264, 364, 364, 484])
     assert n == [4, 1, 2, 0, 2] and status == 1
@@ -113,7 +117,7 @@ def test_work_list_covers_every_chunk_once_longest_first(seed):
     B, S = int(rng.integers(1, 300)), int(rng.integers(1, 5))
     L = int(rng.integers(S, 6000))
     lens = rng.integers(0, L + 1, size=B)
-    plan = reference_plan(B, S, 16, L, 256, PlanOptions(force_chunk=int(rng.choice([0, 64, 256, 1024]))))
+    plan = reference_plan(B, S, 16, L, 256, PlanOptions(force_chunk=int(rng.choice([0, 64, 256, 1024]))), kv_dtype="bf16")
     C = plan["chunk_len"]
     indptr = np.concatenate([[0], np.cumsum(lens)])  # page size 1: one page per row
     n, _, _ = device_plan_arrays(plan, S, L, 1, lens, indptr)
