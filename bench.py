@@ -12,6 +12,15 @@ previous call's cache rows, as in serving where other layers run in between.
 The flush reads rather than writes: a write leaves ~256 MB of dirty lines whose
 write-back would compete with the next call's reads. Prints one JSON line.
 
+The default run (the dense batch-64 workload) also measures every other decode
+workload of the suite the same way, with fewer calls each, and reports them in
+the line's "configs" object: µs per call, decode and merge kernel times, the
+device planner's time (event pair around one plan launch; the plan is made once
+per batch composition and shared by every layer, so it is not part of a call),
+the roofline bound and fraction per call and per decode launch, and the
+counter-measured traffic over the algorithmic bytes where a current profile is
+committed. --no-configs skips them.
+
 Roofline accounting (per decode launch):
   algorithmic bytes = sum_b ctx_b * 576 * e (each cache row read once; e = 2 bf16, 1 fp8)
                       + B*S*H*576*eq (q; eq = 2 bf16, 1 fp8) + B*S*H*512*2 (out) + 4*(B+1) + 4*pages + 4*B (page table, lengths)
@@ -309,6 +318,138 @@ def kvb_bench(args):
     }), flush=True)
 
 
+# The workloads of the per-config lines (one each; the headline workload is the
+# dense batch-64 one above): the tiny two-sequence case, the ragged 256-sequence
+# fp8 batch, the long-context 12-head fp8 decode at batch 1 to 5, and the causal
+# four-token decode.
+CONFIG_WORKLOADS = ("tiny_b2_h16", "ragged_b256_h128_fp8_p64",
+                    *[f"longctx_b{b}_h12_ctx109440_fp8" for b in range(1, 6)],
+                    "causal_mtp4_b128_h16_ctx5200_fp8_p16")
+
+
+def upload_case(case):
+    from mla_paged_latent_02_amd.device import DeviceInputs
+    return DeviceInputs.from_host(
+        q_bits=case.q_bits, cache_raw=case.cache_raw, kv_indptr=case.kv_indptr,
+        kv_page_indices=case.kv_page_indices, context_lens=case.context_lens, batch=case.batch,
+        seqlen_qo=case.seqlen_qo, num_heads=case.num_heads, page_size=case.page_size,
+        max_context_len=case.max_context_len, causal=case.causal, kv_dtype=case.kv_dtype,
+        softmax_scale=case.softmax_scale, kv_scale=case.kv_scale, num_slots=case.num_slots,
+        q_dtype=case.q_dtype, q_scale=case.q_scale)
+
+
+def roofline_for(nbytes, flops, seconds):
+    """The bound the workload's arithmetic intensity puts it under, and the fraction of that peak reached."""
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if flops / nbytes < ridge:
+        gbs = nbytes / seconds / 1e9
+        return {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}
+    tf = flops / seconds / 1e12
+    return {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": tf / MFMA_BF16_PEAK_TFLOPS}
+
+
+def measure_decode(case, workload, steps, warmup, use_flush, plan_reps=20):
+    """Times one workload: plan (device launch, event pairs), then `steps` calls of decode + merge with a
+    read flush before each. Returns the raw measurements and derived rates as a dict."""
+    import numpy as np
+    import torch
+
+    import mla_paged_latent_02_amd as mla
+    from mla_paged_latent_02_amd.device import Decoder
+
+    inp = upload_case(case)
+    stream = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    dec = Decoder(inp, None, 0, stream)
+    torch.cuda.synchronize()
+    plan_wall_us = (time.perf_counter() - t0) * 1e6
+    # the planner re-run on the same workspace writes the same arrays; each run is one device launch
+    plan_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(plan_reps)]
+    for e in plan_ev:
+        e[0].record(stream)
+        mla.decode_plan(inp.params, inp.context_lens, inp.kv_indptr, dec.workspace, None, 0, stream)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    plan_us = float(np.mean([e[0].elapsed_time(e[1]) for e in plan_ev]) * 1e3)
+
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda") if use_flush else None
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        mla.decode(dec.plan, inp.q, inp.cache, inp.kv_indptr, inp.kv_page_indices, inp.context_lens, dec.out,
+                   dec.lse, dec.workspace, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        mla.split_combine(dec.plan, dec.workspace, dec.out, dec.lse, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        if flush is not None:
+            torch.sum(flush, dim=0, out=sink)
+        step()
+    torch.cuda.synchronize()
+    # Timed loop 1 (the reported value): one event pair around each whole call, nothing in between.
+    call_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    wall0 = time.perf_counter()
+    for k in range(steps):
+        if flush is not None:
+            torch.sum(flush, dim=0, out=sink)
+        call_ev[k][0].record(stream)
+        step()
+        call_ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    call_ms = np.array([e[0].elapsed_time(e[1]) for e in call_ev])
+    # Timed loop 2 (the roofline): a third event between the decode and the merge, so that each
+    # kernel has its own duration; the extra event adds a few µs of gap to each call.
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for k in range(steps):
+        if flush is not None:
+            torch.sum(flush, dim=0, out=sink)
+        step(events[k])
+    torch.cuda.synchronize()
+    dec_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    comb_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    del dec, inp, flush
+    torch.cuda.empty_cache()
+
+    nbytes, flops = algorithmic_counts(case)
+    call_us = float(np.mean(call_ms) * 1e3)
+    dec_us = float(np.mean(dec_ms) * 1e3)
+    traffic_bytes = recorded_traffic(workload)
+    return {
+        "call_us": call_us, "call_ms_all": call_ms, "wall_s": wall,
+        "decode_us": dec_us, "combine_us": float(np.mean(comb_ms) * 1e3),
+        "call_us_p10_p50_p90": [float(np.percentile(call_ms, q) * 1e3) for q in (10, 50, 90)],
+        "plan_us": plan_us, "plan_wall_us_first_call": plan_wall_us,
+        "alg_bytes": nbytes, "alg_flops": flops,
+        "per_call": roofline_for(nbytes, flops, call_us * 1e-6),
+        "decode": roofline_for(nbytes, flops, dec_us * 1e-6),
+        "traffic_bytes_per_launch": traffic_bytes,
+        "traffic_over_alg_bytes": None if traffic_bytes is None else traffic_bytes / nbytes,
+    }
+
+
+def config_summary(case, m):
+    """The compact per-config record of the default run."""
+    pc, d = m["per_call"], m["decode"]
+    return {
+        "batch": case.batch, "heads": case.num_heads, "seqlen_qo": case.seqlen_qo,
+        "max_ctx": case.max_context_len, "page_size": case.page_size, "kv_dtype": case.kv_dtype,
+        "causal": case.causal, "us_per_call": m["call_us"], "call_us_p50": m["call_us_p10_p50_p90"][1],
+        "decode_us": m["decode_us"], "combine_us": m["combine_us"], "plan_us": m["plan_us"],
+        "bound": pc["bound"], "frac_per_call": pc["frac"], "frac_decode": d["frac"],
+        "achieved_per_call": pc["achieved"], "unit": pc["unit"],
+        "hbm_tb_per_s_per_call": m["alg_bytes"] / (m["call_us"] * 1e-6) / 1e12,
+        "alg_bytes": m["alg_bytes"], "alg_flops": m["alg_flops"],
+        "counter_traffic_over_alg_bytes": m["traffic_over_alg_bytes"],
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -317,6 +458,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-config lines of the other workloads")
+    ap.add_argument("--config-steps", type=int, default=30, help="timed calls per config of the per-config lines")
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -339,129 +482,84 @@ def main():
         for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
             os.environ[var] = n
 
-    import numpy as np
     import torch
 
-    import mla_paged_latent_02_amd as mla
-    from mla_paged_latent_02_amd.device import Decoder, DeviceInputs
     from mla_synth import WORKLOADS, make_case
 
-    spec = WORKLOADS[args.workload]
-    t_gen = time.perf_counter()
-    case = make_case(**spec)
-    t_gen = time.perf_counter() - t_gen
     torch.cuda.set_device(0)
-    inp = DeviceInputs.from_host(
-        q_bits=case.q_bits, cache_raw=case.cache_raw, kv_indptr=case.kv_indptr,
-        kv_page_indices=case.kv_page_indices, context_lens=case.context_lens, batch=case.batch,
-        seqlen_qo=case.seqlen_qo, num_heads=case.num_heads, page_size=case.page_size,
-        max_context_len=case.max_context_len, causal=case.causal, kv_dtype=case.kv_dtype,
-        softmax_scale=case.softmax_scale, kv_scale=case.kv_scale, num_slots=case.num_slots,
-        q_dtype=case.q_dtype, q_scale=case.q_scale)
-    stream = torch.cuda.current_stream()
-    t0 = time.perf_counter()
-    dec = Decoder(inp, None, 0, stream)
-    torch.cuda.synchronize()
-    plan_us = (time.perf_counter() - t0) * 1e6
-    flush = None if args.no_flush else torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    case = make_case(**WORKLOADS[args.workload])
+    m = measure_decode(case, args.workload, args.steps, args.warmup, not args.no_flush)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        mla.decode(dec.plan, inp.q, inp.cache, inp.kv_indptr, inp.kv_page_indices, inp.context_lens, dec.out,
-                   dec.lse, dec.workspace, stream)
-        if ev is not None:
-            ev[1].record(stream)
-        mla.split_combine(dec.plan, dec.workspace, dec.out, dec.lse, stream)
-        if ev is not None:
-            ev[2].record(stream)
-
-    sink = torch.empty((), dtype=torch.float32, device="cuda")
-    for _ in range(args.warmup):
-        if flush is not None:
-            torch.sum(flush, dim=0, out=sink)
-        step()
-    torch.cuda.synchronize()
-    # Timed loop 1 (the reported value): one event pair around each whole call, nothing in between.
-    call_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    wall0 = time.perf_counter()
-    for k in range(args.steps):
-        if flush is not None:
-            torch.sum(flush, dim=0, out=sink)
-        call_ev[k][0].record(stream)
-        step()
-        call_ev[k][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    call_ms = np.array([e[0].elapsed_time(e[1]) for e in call_ev])
-    call_us = float(np.mean(call_ms) * 1e3)
-    # Timed loop 2 (the roofline): a third event between the decode and the merge, so that each
-    # kernel has its own duration; the extra event adds a few µs of gap to each call.
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for k in range(args.steps):
-        if flush is not None:
-            torch.sum(flush, dim=0, out=sink)
-        step(events[k])
-    torch.cuda.synchronize()
-    dec_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
-    comb_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
-
-    nbytes, flops = algorithmic_counts(case)
-    dec_s = float(np.mean(dec_ms)) * 1e-3
-    achieved_gbs = nbytes / dec_s / 1e9
-    tbs_call = nbytes / (call_us * 1e-6) / 1e12
-    mfma_pct_call = flops / (call_us * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 100
-    ai = flops / nbytes
-    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if ai < ridge:
-        roof = {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved_gbs / HBM_PEAK_GBS}
-    else:
-        tf = flops / dec_s / 1e12
-        roof = {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": tf / MFMA_BF16_PEAK_TFLOPS}
-    traffic_bytes = recorded_traffic(args.workload)
-    roof["traffic"] = None if traffic_bytes is None else traffic_bytes / dec_s / 1e9
-    roof["traffic_bytes_per_launch"] = traffic_bytes
+    roof = dict(m["decode"])
+    roof["traffic"] = (None if m["traffic_bytes_per_launch"] is None
+                       else m["traffic_bytes_per_launch"] / (m["decode_us"] * 1e-6) / 1e9)
+    roof["traffic_bytes_per_launch"] = m["traffic_bytes_per_launch"]
     roof["kernel_source_sha256_16"] = kernel_source_digest()
     roof["mfma_busy_pct_counter"] = recorded_mfma_busy("mla_decode_kernel", args.workload, kernel_source_digest())
     roof["kernel"] = "mla_decode_kernel"
-    roof["kernel_avg_us"] = float(np.mean(dec_ms) * 1e3)
-    roof["alg_bytes"] = nbytes
-    roof["alg_flops"] = flops
+    roof["kernel_avg_us"] = m["decode_us"]
+    roof["alg_bytes"] = m["alg_bytes"]
+    roof["alg_flops"] = m["alg_flops"]
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(case)
 
+    configs = None
+    if not args.no_configs and args.workload == DEFAULT_WORKLOAD:
+        configs = {}
+        for name in CONFIG_WORKLOADS:
+            del case
+            case = make_case(**WORKLOADS[name])
+            configs[name] = config_summary(case, measure_decode(case, name, args.config_steps,
+                                                                min(args.warmup, 5), not args.no_flush))
+            print(json.dumps({"config_done": name, "us_per_call": configs[name]["us_per_call"]}),
+                  file=sys.stderr, flush=True)
+
     result = {
         "metric": METRIC,
-        "value": call_us,
+        "value": m["call_us"],
         "unit": "us",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": float(np.mean(call_ms)),
+        "ms_per_step": m["call_us"] / 1e3,
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("bf16" if case.kv_dtype == "bf16" else
-                  "fp8-e4m3fn query and cache: QK^T on fp8 MFMA, PV on bf16 MFMA" if case.q_dtype != "bf16" else
+        "dtype": ("bf16" if case_dtype_is_bf16(args.workload) else
+                  "fp8-e4m3fn query and cache: QK^T on fp8 MFMA, PV on bf16 MFMA"
+                  if WORKLOADS[args.workload].get("q_dtype", "bf16") != "bf16" else
                   "fp8-e4m3fn cache: QK^T on fp8 MFMA, PV on bf16 MFMA"),
         "data": "synthetic",
-        "config": {"workload": args.workload, "batch": case.batch, "heads": case.num_heads,
-                   "seqlen_qo": case.seqlen_qo, "max_ctx": case.max_context_len, "page_size": case.page_size,
-                   "kv_dtype": case.kv_dtype, "causal": case.causal},
-        "hbm_tb_per_s": tbs_call,
-        "mfma_pct_of_bf16_peak": mfma_pct_call,
-        "decode_us": float(np.mean(dec_ms) * 1e3),
-        "combine_us": float(np.mean(comb_ms) * 1e3),
-        "call_us_p10_p50_p90": [float(np.percentile(call_ms, q) * 1e3) for q in (10, 50, 90)],
-        "plan_us_first_call": plan_us,
-        "wall_s_timed_loop": wall,
-        "flush_between_steps": flush is not None,
+        "config": {"workload": args.workload, **{k: v for k, v in workload_shape(args.workload).items()}},
+        "hbm_tb_per_s": m["alg_bytes"] / (m["call_us"] * 1e-6) / 1e12,
+        "mfma_pct_of_bf16_peak": m["alg_flops"] / (m["call_us"] * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 100,
+        "decode_us": m["decode_us"],
+        "combine_us": m["combine_us"],
+        "plan_us": m["plan_us"],
+        "call_us_p10_p50_p90": m["call_us_p10_p50_p90"],
+        "plan_wall_us_first_call": m["plan_wall_us_first_call"],
+        "wall_s_timed_loop": m["wall_s"],
+        "flush_between_steps": not args.no_flush,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "configs": configs,
     }
     print(json.dumps(result), flush=True)
+
+
+def case_dtype_is_bf16(workload):
+    from mla_synth import WORKLOADS
+    return WORKLOADS[workload]["kv_dtype"] == "bf16"
+
+
+def workload_shape(workload):
+    """The shape fields of a workload, as the config object names them."""
+    from mla_synth import WORKLOADS
+    w = WORKLOADS[workload]
+    ctx = w["ctx"]
+    return {"batch": w["batch"], "heads": w["num_heads"], "seqlen_qo": w["seqlen_qo"],
+            "max_ctx": (ctx[2] if isinstance(ctx, tuple) else max(ctx) if isinstance(ctx, list) else ctx),
+            "page_size": w["page_size"], "kv_dtype": w["kv_dtype"], "causal": bool(w.get("causal", False))}
 
 
 if __name__ == "__main__":
