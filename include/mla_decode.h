@@ -51,11 +51,11 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 5
+#define MLA_ABI_VERSION 6
 #define MLA_ROW_DIM 576    /* q / cache row width: 512 latent + 64 rope */
 #define MLA_LATENT_DIM 512 /* V width = output width */
 #define MLA_MAX_SEQLEN_QO 8
-#define MLA_PLAN_MAGIC 0x4d4c4131u
+#define MLA_PLAN_MAGIC 0x4d4c4132u
 
 typedef enum {
   MLA_OK = 0,
@@ -74,11 +74,12 @@ typedef enum { MLA_KV_BF16 = 0, MLA_KV_FP8_E4M3FN = 1 } mla_kv_dtype_t;
  * byte times one per-tensor q_scale. It needs an fp8 cache. */
 typedef enum { MLA_Q_BF16 = 0, MLA_Q_FP8_E4M3FN = 1 } mla_q_dtype_t;
 
-/* Status-word bits written to the workspace by the device (see ws_status_offset). */
-#define MLA_DEV_CTX_TOO_SHORT 1u    /* context_lens[b] < seqlen_qo      */
-#define MLA_DEV_CTX_TOO_LONG 2u     /* context_lens[b] > max_context_len */
-#define MLA_DEV_TOO_FEW_PAGES 4u    /* page list shorter than ceil(ctx/page_size) */
+/* Status-word bits written to the workspace by the device (word 0 at ws_status_offset). */
+#define MLA_DEV_CTX_TOO_SHORT 1u     /* context_lens[b] < seqlen_qo      */
+#define MLA_DEV_CTX_TOO_LONG 2u      /* context_lens[b] > max_context_len */
+#define MLA_DEV_TOO_FEW_PAGES 4u     /* page list shorter than ceil(ctx/page_size) */
 #define MLA_DEV_PAGE_OUT_OF_RANGE 8u /* a page index >= num_slots / page_size (or < 0) */
+#define MLA_DEV_STALE_PLAN 16u       /* mla_decode saw a context length of another chunk count than planned */
 
 /* Shape and numeric parameters of one decode call. */
 typedef struct {
@@ -86,7 +87,7 @@ typedef struct {
   int32_t seqlen_qo;       /* S, 1..8 query tokens per sequence */
   int32_t num_heads;       /* H >= 1 */
   int32_t page_size;       /* P >= 1 cache rows per page */
-  int32_t max_context_len; /* upper bound of context_lens (sizes the grid and workspace) */
+  int32_t max_context_len; /* upper bound of context_lens (sizes the chunks and workspace) */
   int32_t causal;          /* 0 or 1: token s sees ctx - S + 1 + s rows */
   int32_t kv_dtype;        /* mla_kv_dtype_t */
   float softmax_scale;     /* multiplies q . k */
@@ -98,7 +99,7 @@ typedef struct {
 
 /* Tunables of the work split, per tile class (tile rows 16, 32, 64, 128). */
 typedef struct {
-  int32_t wg_per_cu[4]; /* target workgroups per CU */
+  int32_t wg_per_cu[4]; /* persistent workgroups per CU (capped at what the class's kernel holds) */
   int32_t chunk_min[4]; /* chunk length bounds in cache rows, multiples of 64 */
   int32_t chunk_max[4];
   int32_t force_chunk;  /* 0 = use the rule; else this chunk length (multiple of 64) */
@@ -115,17 +116,18 @@ typedef struct {
   int32_t rows_per_group;  /* hpg * S valid rows per tile */
   int32_t tile_rows;       /* 16, 32, 64 or 128 */
   int32_t tile_class;      /* log2(tile_rows / 16) */
-  int32_t chunk_len;       /* C, cache rows per workgroup, multiple of 64 */
+  int32_t chunk_len;       /* C, cache rows per work item, multiple of 64 */
   int32_t max_chunks;      /* ceil(max_context_len / C) */
-  int32_t grid[3];         /* decode grid: (work_capacity * G, 1, 1) */
+  int32_t wg_per_cu;       /* occupancy used: min(options.wg_per_cu[class], what the kernel holds) */
+  int32_t num_workgroups;  /* W = num_cu * wg_per_cu: the persistent decode grid */
   int64_t partial_capacity_records; /* B * G * max_chunks */
   int64_t work_capacity;            /* B * max_chunks: entries of the work list */
-  uint64_t ws_status_offset;   /* uint32 [4]: status bits, work-item count, 0, 0 (bytes from workspace start) */
+  uint64_t ws_status_offset;   /* uint32 [4]: status bits, item count, task counter (W between calls), 0 */
   uint64_t ws_nchunks_offset;  /* int32 [B]: chunks of each sequence (0 = invalid sequence) */
   uint64_t ws_partbase_offset; /* int32 [B]: first partial record of each sequence */
   uint64_t ws_part_out_offset; /* float [records][rows_per_group][512]: normalised partial outputs */
   uint64_t ws_part_lse_offset; /* float [records][rows_per_group]: partial lse, base-2 log */
-  uint64_t ws_work_offset;     /* int32 [work_capacity][2]: (sequence, chunk) work items in dispatch order */
+  uint64_t ws_work_offset;     /* int32 [work_capacity][2]: (sequence, chunk) work items, longest first */
   uint64_t ws_bytes;           /* total workspace bytes needed */
 } mla_plan_t;
 
@@ -135,52 +137,77 @@ int32_t mla_abi_version(void);
 /* Human-readable text of a status code (static storage). */
 const char* mla_status_string(mla_status_t status);
 
-/* Fills *out with the default tunables: wg_per_cu {1, 1, 2, 1} (the LDS that
- * each tile class's kernel holds per workgroup), chunk_min {256, 256, 256, 128},
- * chunk_max {8192, 8192, 4096, 6144}, force_chunk 0. */
+/* Fills *out with the default tunables: wg_per_cu {1, 1, 2, 1} (the 64-row kernel
+ * runs at occupancy 2, as the pages' m16x4 kernel does: "HK MLA: MI35x m16x8
+ * retune, new m16x4 kernel, page_size + mask support", Summary);
+ * chunk_min {256, 256, 256, 128}, chunk_max {8192, 8192, 4096, 6144}, force_chunk 0. */
 void mla_plan_options_default(mla_plan_options_t* out);
 
 /*
  * Host half of the planner: validates params and computes the plan (tile
- * grouping, chunk length, grid, workspace layout) with no device work and no
- * HIP call when num_cu > 0. num_cu <= 0 asks the current device for its CU
- * count. options may be NULL (defaults). Rule ("perf(mla): chunk the non-FP4
- * gather_kv_b_proj over KV", description: chunk grid from the longest
- * sequence; "HK MLA ..." Summary: rows = heads x query tokens, num_cu clusters):
+ * grouping, persistent grid, chunk length, workspace layout) with no device
+ * work and no HIP call when num_cu > 0. num_cu <= 0 asks the current device for
+ * its CU count. options may be NULL (defaults). Sources: "HK MLA: MI35x m16x8
+ * retune, new m16x4 kernel, page_size + mask support", Summary and file table
+ * (a persistent decode kernel whose metadata is sized for num_cu clusters,
+ * doubled when the 64-row kernel runs at occupancy 2; heads x query tokens
+ * stacked into 64- or 128-row tiles) and "perf(mla): chunk the non-FP4
+ * gather_kv_b_proj over KV", description (KV chunks sized from the longest
+ * sequence, so that few long sequences still fill the device). Rule:
  *   hpg = min(H, 128/S); G = ceil(H/hpg); TR = smallest of 16/32/64/128 >= hpg*S
+ *   wg_per_cu = min(options.wg_per_cu[class], fit), fit = workgroups per CU that the
+ *               class's decode kernel holds for the cache type (2 for fp8 64-row tiles, else 1)
+ *   W = num_cu * wg_per_cu
  *   C = force_chunk or clamp(roundup(ceil(Lmax / want), 64), chunk_min, chunk_max),
- *       want = max(1, floor(num_cu * min(wg_per_cu, fit) / (B*G))), fit = workgroups per CU that
- *       the decode kernel of the class and cache type holds: 2 for fp8 64-row tiles, else 1
- *   max_chunks = ceil(Lmax / C), work_capacity = B * max_chunks, grid = (work_capacity * G, 1, 1)
+ *       want = max(1, floor(W / (B*G)))
+ *   max_chunks = ceil(Lmax / C), work_capacity = B * max_chunks
+ * Returns MLA_ERR_UNSUPPORTED when the task count B * max_chunks * G or a
+ * workspace index would not fit the device's 32-bit arithmetic.
  */
 mla_status_t mla_decode_plan_host(const mla_decode_params_t* params, const mla_plan_options_t* options,
                                   int32_t num_cu, mla_plan_t* out_plan);
 
-/* Workspace bytes for a call shape (0 if params or options are invalid). */
+/* Workspace bytes for a call shape (0 if params or options are invalid). Same
+ * rule and sources as mla_decode_plan_host; the caller allocates this many bytes. */
 size_t mla_decode_workspace_size(const mla_decode_params_t* params, const mla_plan_options_t* options,
                                  int32_t num_cu);
 
 /*
- * Full planner: the host half above, then one device launch that, per
- * sequence, validates context_lens[b] (S <= ctx <= max_context_len, enough
- * pages), writes n_b = ceil(ctx_b / C) (0 if invalid), the exclusive prefix
- * sum of partial records, the status word, and the work list: the decode
- * workgroups' items (b, chunk) in dispatch order, longest first so that the
- * last workgroups on the CUs are short (a scheduling choice of this library):
- * every full chunk (exactly C rows) in (b, chunk) order; then each sequence's
- * partial last chunk (r = ctx - (n_b - 1) C rows) by length class
- * floor(16 r / C), longest class first, ties by b; then (b, -1) for every
- * invalid sequence. The item count goes to status word 1. d_context_lens [B]
- * and d_kv_indptr [B+1] are int32 device arrays. The device arrays stay valid
- * for every mla_decode / mla_split_combine call with the same context lengths.
+ * Full planner: the host half above, then one device launch that builds the
+ * persistent kernel's metadata ("HK MLA: MI35x m16x8 retune, new m16x4 kernel,
+ * page_size + mask support", file table: device-built metadata; "perf(mla):
+ * chunk the non-FP4 gather_kv_b_proj over KV", description: KV chunks, none
+ * past its sequence's end). Per sequence it validates context_lens[b]
+ * (S <= ctx <= max_context_len, enough pages), writes n_b = ceil(ctx_b / C) (0
+ * if invalid) and the exclusive prefix sum of partial records; it writes the
+ * work list, items (b, chunk) longest first (a scheduling choice of this
+ * library): every full chunk (exactly C rows) in (b, chunk) order, then each
+ * sequence's partial last chunk (r = ctx - (n_b - 1) C rows) by length class
+ * floor(16 r / C), longest class first, ties by b, then (b, -1) for every
+ * invalid sequence; and the status words: the bits, the item count, the task
+ * counter's start W and a reserved 0. d_context_lens [B] and
+ * d_kv_indptr [B+1] are int32 device arrays. The plan stays valid for every
+ * mla_decode / mla_split_combine call whose context lengths keep each
+ * sequence's chunk count; mla_decode sets MLA_DEV_STALE_PLAN when one does not.
  */
 mla_status_t mla_decode_plan(const mla_decode_params_t* params, const mla_plan_options_t* options,
                              int32_t num_cu, const int32_t* d_context_lens, const int32_t* d_kv_indptr,
                              void* d_workspace, size_t workspace_bytes, void* stream, mla_plan_t* out_plan);
 
 /*
- * Decode attention over the paged cache. Workgroup x runs work item x / G for
- * head group x % G; workgroups past the item count exit at once.
+ * Decode attention over the paged cache ("HK MLA: MI35x m16x8 retune, new m16x4
+ * kernel, page_size + mask support", Summary: paged latent cache, any page
+ * size, causal mask for multi-token queries, persistent kernel; "[Perf][Kimi-K3]
+ * Cut MLA decode concat/cache epilogue latency", Purpose: absorbed query and
+ * 576-wide latent rows). A persistent grid of plan->num_workgroups workgroups
+ * walks the tasks of the work list: task t is item t / G for head group t % G.
+ * Workgroup x first runs task (x mod 8) * (W / 8) + x / 8 when W is a multiple
+ * of 8 (x otherwise), then takes the next untaken task from the workspace's
+ * task counter (a device-scope atomic) as each task's last block starts, until
+ * none is left, so the longest work goes first to whichever workgroup is about
+ * to be free; the workgroup that takes the call's last counter value sets the
+ * counter back to W for the next call. Calls sharing one workspace must not
+ * overlap (stream-order them).
  *   d_q              [B, S, H, 576], contiguous: bf16, or e4m3fn bytes (value = byte * q_scale)
  *                    when params.q_dtype is MLA_Q_FP8_E4M3FN
  *   d_kv_cache       [num_slots, 576] bf16 or fp8 e4m3fn bytes, contiguous
@@ -211,10 +238,11 @@ mla_status_t mla_split_combine(const mla_plan_t* plan, void* d_workspace, size_t
 
 /*
  * Test hook: synchronously copies the planner's device arrays to host memory
- * (any pointer may be NULL). h_nchunks and h_partbase hold B int32 each.
+ * (any pointer may be NULL). h_nchunks and h_partbase hold B int32 each,
+ * h_status the 4 status words.
  */
-mla_status_t mla_debug_read_plan_arrays(const mla_plan_t* plan, const void* d_workspace,
-                                        int32_t* h_nchunks, int32_t* h_partbase, uint32_t* h_status);
+mla_status_t mla_debug_read_plan_arrays(const mla_plan_t* plan, const void* d_workspace, int32_t* h_nchunks,
+                                        int32_t* h_partbase, uint32_t* h_status);
 
 /*
  * Test hook: synchronously copies the work list to host memory. *h_count

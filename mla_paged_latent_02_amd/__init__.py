@@ -36,6 +36,7 @@ DEV_CTX_TOO_SHORT = 1
 DEV_CTX_TOO_LONG = 2
 DEV_TOO_FEW_PAGES = 4
 DEV_PAGE_OUT_OF_RANGE = 8
+DEV_STALE_PLAN = 16
 
 # Every function the header declares, in declaration order.
 EXPORTED = ["mla_abi_version", "mla_status_string", "mla_plan_options_default", "mla_decode_plan_host",
@@ -75,7 +76,8 @@ class Plan(ctypes.Structure):
     _fields_ = [("magic", ctypes.c_uint32), ("num_cu", ctypes.c_int32), ("params", DecodeParams),
                 ("options", PlanOptions), ("heads_per_group", ctypes.c_int32), ("num_groups", ctypes.c_int32),
                 ("rows_per_group", ctypes.c_int32), ("tile_rows", ctypes.c_int32), ("tile_class", ctypes.c_int32),
-                ("chunk_len", ctypes.c_int32), ("max_chunks", ctypes.c_int32), ("grid", ctypes.c_int32 * 3),
+                ("chunk_len", ctypes.c_int32), ("max_chunks", ctypes.c_int32), ("wg_per_cu", ctypes.c_int32),
+                ("num_workgroups", ctypes.c_int32),
                 ("partial_capacity_records", ctypes.c_int64), ("work_capacity", ctypes.c_int64),
                 ("ws_status_offset", ctypes.c_uint64), ("ws_nchunks_offset", ctypes.c_uint64),
                 ("ws_partbase_offset", ctypes.c_uint64), ("ws_part_out_offset", ctypes.c_uint64),
@@ -251,16 +253,16 @@ def gather_kv_b_proj(params: KvbParams, kv_cache, kv_indptr, kv_page_indices, cu
 
 
 def read_plan_arrays(plan: Plan, workspace):
-    """(n_chunks list, partial bases list, status word) copied synchronously to the host."""
+    """(n_chunks list, partial bases list, the four status words) copied synchronously to the host."""
     B = plan.params.batch
     n = (ctypes.c_int32 * B)()
     base = (ctypes.c_int32 * B)()
-    status = ctypes.c_uint32(0)
+    status = (ctypes.c_uint32 * 4)()
     st = _lib.mla_debug_read_plan_arrays(ctypes.byref(plan), _ptr(workspace), ctypes.cast(n, ctypes.c_void_p),
-                                         ctypes.cast(base, ctypes.c_void_p), ctypes.cast(ctypes.byref(status), ctypes.c_void_p))
+                                         ctypes.cast(base, ctypes.c_void_p), ctypes.cast(status, ctypes.c_void_p))
     if st != MLA_OK:
         raise MlaError("mla_debug_read_plan_arrays", st)
-    return list(n), list(base), status.value
+    return list(n), list(base), list(status)
 
 
 def read_work_list(plan: Plan, workspace):
@@ -278,6 +280,7 @@ def plan_to_dict(plan: Plan) -> dict:
     return {
         "heads_per_group": plan.heads_per_group, "num_groups": plan.num_groups,
         "rows_per_group": plan.rows_per_group, "tile_rows": plan.tile_rows, "tile_class": plan.tile_class,
-        "chunk_len": plan.chunk_len, "max_chunks": plan.max_chunks, "grid": tuple(plan.grid),
+        "chunk_len": plan.chunk_len, "max_chunks": plan.max_chunks, "wg_per_cu": plan.wg_per_cu,
+        "num_workgroups": plan.num_workgroups, "grid": (plan.num_workgroups, 1, 1),
         "partial_capacity_records": plan.partial_capacity_records, "work_capacity": plan.work_capacity,
     }

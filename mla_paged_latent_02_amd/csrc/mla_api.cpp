@@ -23,7 +23,6 @@ mla_status_t mla_decode_plan(const mla_decode_params_t* params, const mla_plan_o
   mla_plan_t plan;
   mla_status_t st = mla_decode_plan_host(params, options, num_cu, &plan);
   if (st != MLA_OK) return st;
-  if (int64_t(plan.params.batch) * plan.num_groups > 65535) return MLA_ERR_UNSUPPORTED;
   if (plan.params.num_slots >= (int64_t(1) << 31)) return MLA_ERR_UNSUPPORTED;
   if (workspace_bytes < plan.ws_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
   mla::PlanArgs a;
@@ -39,6 +38,7 @@ mla_status_t mla_decode_plan(const mla_decode_params_t* params, const mla_plan_o
   a.page_size = plan.params.page_size;
   a.chunk_len = plan.chunk_len;
   a.num_groups = plan.num_groups;
+  a.num_workgroups = plan.num_workgroups;
   if (mla::launch_plan(a, stream) != 0) return MLA_ERR_HIP;
   *out_plan = plan;
   return MLA_OK;
@@ -77,13 +77,14 @@ mla_status_t mla_decode(const mla_plan_t* plan, const void* d_q, const void* d_k
   a.num_groups = plan->num_groups;
   a.rows_per_group = plan->rows_per_group;
   a.chunk_len = plan->chunk_len;
+  a.num_workgroups = plan->num_workgroups;
+  a.work_capacity = int32_t(plan->work_capacity);
   a.causal = p.causal;
   // both per-tensor scales multiply every score: folded into the softmax scale
   a.score_scale_log2 =
       float(double(p.softmax_scale) * double(p.kv_scale) * double(p.q_scale) * 1.4426950408889634);
   a.out_scale = p.kv_scale;
-  if (mla::launch_decode(a, p.kv_dtype, p.q_dtype == MLA_Q_FP8_E4M3FN, plan->tile_class, plan->grid[0],
-                         plan->grid[1], plan->grid[2], stream) != 0)
+  if (mla::launch_decode(a, p.kv_dtype, p.q_dtype == MLA_Q_FP8_E4M3FN, plan->tile_class, stream) != 0)
     return MLA_ERR_HIP;
   return MLA_OK;
 }
@@ -107,7 +108,6 @@ mla_status_t mla_split_combine(const mla_plan_t* plan, void* d_workspace, size_t
   a.heads_per_group = plan->heads_per_group;
   a.num_groups = plan->num_groups;
   a.rows_per_group = plan->rows_per_group;
-  a.cols_per_wg = 0;
   if (mla::launch_combine(a, plan->max_chunks, stream) != 0) return MLA_ERR_HIP;
   return MLA_OK;
 }
@@ -123,7 +123,7 @@ mla_status_t mla_debug_read_plan_arrays(const mla_plan_t* plan, const void* d_wo
     return MLA_ERR_HIP;
   if (h_partbase && hipMemcpy(h_partbase, ws + plan->ws_partbase_offset, nb, hipMemcpyDeviceToHost) != hipSuccess)
     return MLA_ERR_HIP;
-  if (h_status && hipMemcpy(h_status, ws + plan->ws_status_offset, 4, hipMemcpyDeviceToHost) != hipSuccess)
+  if (h_status && hipMemcpy(h_status, ws + plan->ws_status_offset, 16, hipMemcpyDeviceToHost) != hipSuccess)
     return MLA_ERR_HIP;
   return MLA_OK;
 }

@@ -9,9 +9,10 @@ namespace mla {
 
 constexpr int kRowDim = MLA_ROW_DIM;       // 576
 constexpr int kLatentDim = MLA_LATENT_DIM; // 512
-constexpr int kBlockRows = 64;             // cache rows per pipeline block; chunks are multiples
+constexpr int kBlockRows = 64;             // chunks are multiples of this many cache rows
 constexpr int kMaxTileRows = 128;
 constexpr int kMaxSeqlenQo = MLA_MAX_SEQLEN_QO;
+constexpr int kNumXcd = 8;                 // the hardware deals consecutive workgroups to 8 XCDs in turn
 
 // Everything one decode launch needs, passed by value.
 struct DecodeArgs {
@@ -23,7 +24,7 @@ struct DecodeArgs {
   const int32_t* nchunks;       // [B] from the planner
   const int32_t* partbase;      // [B] from the planner
   const int32_t* work;          // [capacity][2] (sequence, chunk) items from the planner
-  uint32_t* status;             // [0] status bits, [1] work-item count
+  uint32_t* status;             // [0] status bits, [1] item count, [2] task counter, [3] finished workgroups
   uint16_t* out;                // bf16 [B, S, H, 512]
   float* lse;                   // [B, S, H] or null
   float* part_out;              // [records][rows][512]
@@ -32,8 +33,10 @@ struct DecodeArgs {
   uint32_t page_div_magic;      // floor((2^32 - 1) / page_size): q = umulhi(n, magic), then one correction
   int32_t batch, seqlen_qo, num_heads, page_size;
   int32_t heads_per_group, num_groups, rows_per_group, chunk_len;
+  int32_t num_workgroups;       // W: the persistent grid
+  int32_t work_capacity;        // entries of the work list
   int32_t causal;
-  float score_scale_log2;       // softmax_scale * kv_scale * log2(e)
+  float score_scale_log2;       // softmax_scale * kv_scale * q_scale * log2(e)
   float out_scale;              // kv_scale
 };
 
@@ -45,7 +48,6 @@ struct CombineArgs {
   uint16_t* out;
   float* lse;
   int32_t batch, seqlen_qo, num_heads, heads_per_group, num_groups, rows_per_group;
-  int32_t cols_per_wg;  // 512 / column blocks
 };
 
 struct PlanArgs {
@@ -55,13 +57,16 @@ struct PlanArgs {
   int32_t* partbase;
   int32_t* work;
   uint32_t* status;
-  int32_t batch, seqlen_qo, max_context_len, page_size, chunk_len, num_groups;
+  int32_t batch, seqlen_qo, max_context_len, page_size, chunk_len, num_groups, num_workgroups;
 };
 
 // Launchers (mla_kernels.hip). Return hipError_t as int.
 int launch_plan(const PlanArgs& a, void* stream);
-int launch_decode(const DecodeArgs& a, int kv_dtype, bool q_fp8, int tile_class, int grid_x, int grid_y, int grid_z,
-                  void* stream);
+int launch_decode(const DecodeArgs& a, int kv_dtype, bool q_fp8, int tile_class, void* stream);
 int launch_combine(const CombineArgs& a, int max_chunks, void* stream);
+
+// Workgroups per CU that the decode kernel of this cache type, query type and
+// tile class holds (its LDS and its waves): the occupancy the planner can ask for.
+int decode_wg_per_cu_fit(int kv_dtype, bool q_fp8, int tile_class);
 
 }  // namespace mla

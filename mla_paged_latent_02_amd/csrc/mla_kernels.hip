@@ -21,6 +21,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "mla_internal.h"
 
@@ -98,7 +99,8 @@ __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
 // chunk) order, then partial last chunks by length class (longest first,
 // ties by sequence), then one NaN-fill item per invalid sequence. Ranks
 // within a class follow sequence order (wave ballots plus per-wave counts),
-// so the list is deterministic.
+// so the list is deterministic. Last, the status words, with the persistent
+// decode grid's task counter at its start W.
 constexpr int kLengthClasses = 16;
 constexpr int kCats = kLengthClasses + 1;  // length classes, then invalid sequences
 
@@ -190,14 +192,25 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(PlanArgs a) {
       scan_full[tid] += v1;
       __syncthreads();
     }
+    // the tile's full chunks, spread over all threads: item i of the tile is chunk
+    // i - (first item of j) of the tile's sequence j, the first j whose inclusive count
+    // exceeds i (a long sequence's chunks are not written by one thread alone)
+    const int32_t tile_full = scan_full[255];
+    for (int i = tid; i < tile_full; i += 256) {
+      int lo = 0, hi = 255;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (scan_full[mid] > i) hi = mid; else lo = mid + 1;
+      }
+      const int32_t first = lo > 0 ? scan_full[lo - 1] : 0;
+      i32x2_t item;
+      item[0] = base + lo;
+      item[1] = i - first;
+      *(i32x2_t*)(a.work + 2 * (int64_t)(carry_full + i)) = item;
+    }
     if (b < a.batch) {
       a.nchunks[b] = w.n;
       a.partbase[b] = carry_pb + scan_pb[tid] - contrib;
-      const int32_t p0 = carry_full + scan_full[tid] - w.nfull;
-      for (int c = 0; c < w.nfull; ++c) {
-        a.work[2 * (p0 + c)] = b;
-        a.work[2 * (p0 + c) + 1] = c;
-      }
       if (w.cat >= 0) {
         int32_t pos = cat_base[w.cat] + cat_carry[w.cat] + rank;
         for (int v = 0; v < wave; ++v) pos += cat_wave[v][w.cat];
@@ -220,8 +233,8 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(PlanArgs a) {
   }
   if (tid == 0) {
     a.status[0] = bad_or[0];
-    a.status[2] = 0;
-    a.status[3] = 0;
+    a.status[2] = (uint32_t)a.num_workgroups;  // the task counter: workgroup x's first task is below W
+    a.status[3] = 0;                           // reserved
   }
 }
 
@@ -287,6 +300,16 @@ __device__ __forceinline__ void wait_vmcnt_blocks(int k) {
   } else {
     wait_vmcnt<C>();
   }
+}
+
+// A lane's byte offset within a cache row's rope tail, made opaque to the
+// compiler where the tail DMA's address is formed, so that it is computed there
+// as a 32-bit value rather than hoisted out of the block loop and held as a
+// 64-bit one (which spilled in the 128-row fp8 kernel, and a reload from
+// scratch makes the next wait drain every DMA in flight).
+__device__ __forceinline__ uint32_t lane_offset(uint32_t off) {
+  asm volatile("" : "+v"(off));
+  return off;
 }
 
 // Page-gathered loads of one chunk's cache rows, in blocks of BN rows, into
@@ -385,7 +408,7 @@ struct BlockGather {
     const uint32_t stage_off = (uint32_t)(blk % NS) * L::kBlockBytes;
     const int r = wave * RPW + m * kTailRowsPerInst + trow;
     const int logical = tslot ^ L::tail_xor(r);
-    const uint8_t* src = cache + (int64_t)sv * L::kRowBytes + L::kMainBytes + (logical << 4);
+    const uint8_t* src = cache + (int64_t)sv * L::kRowBytes + lane_offset(L::kMainBytes + (logical << 4));
     const uint32_t dst = __builtin_amdgcn_readfirstlane(
         lds_base + stage_off + (uint32_t)(L::kTailBase + (wave * RPW + m * kTailRowsPerInst) * L::kTailBytes));
     if (m * kTailRowsPerInst + trow < RPW) dma16(src, dst);
@@ -616,46 +639,55 @@ struct DecodeCfg {
   static constexpr bool kMergeSpread = KW > 1 && kWaves * kStateBytes <= kRingBytes;
   static constexpr int kMergeWaves = KW == 1 ? 0 : kMergeSpread ? kWaves : (KW - 1) * HW;
   static constexpr int kMergeBytes = kMergeWaves * kStateBytes;
-  static constexpr int kLdsBytes = kRingBytes > kMergeBytes ? kRingBytes : kMergeBytes;
-  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+  // then two int32 slots through which the next task's index passes to every wave
+  static constexpr int kTaskSlotBase = kRingBytes > kMergeBytes ? kRingBytes : kMergeBytes;
+  static constexpr int kLdsBytes = kTaskSlotBase + 16;
+  static_assert(kTaskSlotBase % 16 == 0 && kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
+// The next untaken task of the list: a device-scope vector atomic on the task
+// counter (the planner starts it at W, the grid's first tasks being below W).
+__device__ __forceinline__ int take_task(const DecodeArgs& a) {
+  return (int)__hip_atomic_fetch_add(a.status + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One task: attention of head group grp's tile over KV chunk `chunk` of
+// sequence b (a work item of the planner's list); the output for a
+// single-chunk sequence, else the chunk's partial record. Lane 0 of wave 0
+// takes the workgroup's next task from the counter into nxt as the task's last
+// block starts, so that the workgroup takes work when it is about to be free
+// and the counter's round trip overlaps that block and the epilogue.
 // QF8 (fp8 cache only): the query is e4m3fn bytes; its latent dims go to the
 // fp8 MFMA as they are (one term, unit block scale; the per-tensor q scale is
 // folded into the softmax scale) and its rope dims are widened exactly to bf16.
-template <bool FP8, int HW, int KW, int NS, int WPE, int KD, int VD, int QC, bool QF8 = false>
-__global__ __launch_bounds__(HW * KW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
-void mla_decode_kernel(DecodeArgs a) {
+template <bool FP8, int HW, int KW, int NS, int WPE, int KD, int VD, int QC, bool QF8>
+__device__ __forceinline__ void decode_task(const DecodeArgs& a, LDS_PTR(uint8_t) lds, int b, int chunk, int grp,
+                                            int& nxt) {
   static_assert(FP8 || !QF8, "an fp8 query needs an fp8 cache");
   using Cfg = DecodeCfg<FP8, HW, KW, NS>;
   using L = typename Cfg::L;
   constexpr int NW = Cfg::kWaves;
   constexpr int BN = Cfg::kBlockN;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::kLdsBytes];
-  LDS_PTR(uint8_t) lds = (LDS_PTR(uint8_t))smem;
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keep it scalar
+  // Opaque to the compiler across tasks, so that what is derived from the
+  // thread index is computed inside each task rather than kept in registers
+  // around the task loop (the gather and MFMA loop needs them all).
+  int tid = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep it scalar
   const int hw = wave % HW;   // head tile
   const int kw = wave / HW;   // row slice of each block
   const int i16 = lane & 15;  // MFMA column: head row within the wave's 16-row tile
   const int g4 = lane >> 4;   // MFMA k-group
 
-  // ---- work item: workgroup x runs item x / G of the planner's list for head group x % G.
-  // Every load before the first cache row is a cold round trip, so they go in
-  // three dependent batches: the list count with the item (the list holds
-  // grid / G entries, so an item past the count is still in bounds), then the
-  // sequence's fields, then its first page ids together with the query. The
-  // empty asm statements keep the compiler from spreading a batch over
-  // several waits.
-  const int item = (int)(blockIdx.x / (unsigned)a.num_groups);
-  const int grp = (int)blockIdx.x - item * a.num_groups;
-  const int count = (int)a.status[1];
-  const int b = a.work[2 * item];
-  const int chunk = a.work[2 * item + 1];
-  asm volatile("" ::"s"(count), "s"(b), "s"(chunk));
-  if (item >= count) return;  // past the list
-  if (chunk < 0) {            // invalid sequence: NaN rows
+  // ---- work item (b, chunk), loaded by the caller. Every load before the first
+  // cache row is a cold round trip, so they go in three dependent batches: the
+  // item, then the sequence's fields, then its first page ids together with the
+  // query. The empty asm statements keep the compiler from spreading a batch
+  // over several waits.
+  if (chunk < 0) {  // invalid sequence: NaN rows
+    if (wave == 0 && lane == 0) nxt = take_task(a);
     fill_invalid_rows(a, b, grp, wave, NW, lane);
     return;
   }
@@ -664,6 +696,9 @@ void mla_decode_kernel(DecodeArgs a) {
   const int n_b = a.nchunks[b];
   const int rec_base = a.partbase[b];
   asm volatile("" ::"s"(ctx), "s"(page_base), "s"(n_b), "s"(rec_base));
+  // a context that grew past the planned chunk count would lose its last rows: flag the plan
+  if ((ctx + a.chunk_len - 1) / a.chunk_len != n_b && chunk == 0 && grp == 0 && wave == 0 && lane == 0)
+    atomicOr(a.status, MLA_DEV_STALE_PLAN);
 
   const int c_start = chunk * a.chunk_len;
   const int c_end = min(c_start + a.chunk_len, ctx);
@@ -820,6 +855,8 @@ void mla_decode_kernel(DecodeArgs a) {
     gather.wait(blk);
     __syncthreads();
     gather.advance(blk);
+    // the last block issues no gather: the counter's atomic is the youngest memory operation
+    if (blk == nblk - 1 && wave == 0 && lane == 0) nxt = take_task(a);
     LDS_PTR(uint8_t) stage = lds + (uint32_t)(blk % NS) * L::kBlockBytes;
     // this wave's 32 rows of the block: main rows at mstage, rope tails at tstage
     LDS_PTR(uint8_t) mstage = stage + (uint32_t)(kw * 32 * L::kMainStride);
@@ -1036,6 +1073,70 @@ void mla_decode_kernel(DecodeArgs a) {
   }
 }
 
+// The persistent decode kernel: a grid of W = num_cu x occupancy workgroups
+// walks the tasks of the planner's list (task t: item t / G, head group t % G).
+// Workgroup x first runs task first(x) (consecutive tasks on one XCD: the
+// hardware deals consecutive workgroups to the 8 XCDs in turn, so the head
+// groups and chunks of one sequence share an L2), then the next untaken task
+// of the list from the workspace's task counter (a device-scope vector atomic;
+// the planner starts it at W), taken as each task's last block starts, until
+// the list is done: the longest work goes first, to whichever workgroup is
+// about to be free. The task index passes between waves through two LDS slots
+// used in turn. Every finished task takes one value from the counter, so one
+// call's values are exactly W .. W + tasks - 1: the workgroup that gets the
+// last one knows that every other has taken its last, and sets the counter
+// back to W for the next call.
+template <bool FP8, int HW, int KW, int NS, int WPE, int KD, int VD, int QC, bool QF8 = false>
+__global__ __launch_bounds__(HW * KW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void mla_decode_kernel(DecodeArgs a) {
+  using Cfg = DecodeCfg<FP8, HW, KW, NS>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::kLdsBytes];
+  LDS_PTR(uint8_t) lds = (LDS_PTR(uint8_t))smem;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = a.num_workgroups;
+  const int x = (int)blockIdx.x;
+  const int G = a.num_groups;
+  int task = W % kNumXcd ? x : (x % kNumXcd) * (W / kNumXcd) + x / kNumXcd;
+  // the item count with the first task's item, in one batch (the item index is clamped to
+  // the list's capacity, so a workgroup past the list still reads in bounds)
+  const int n_items = (int)a.status[1];
+  const int item0 = min(task / G, a.work_capacity - 1);
+  int b = a.work[2 * item0];
+  int chunk = a.work[2 * item0 + 1];
+  asm volatile("" ::"s"(n_items), "s"(b), "s"(chunk));
+  const int n_tasks = n_items * G;
+  for (int k = 0; task < n_tasks; ++k) {
+    int nxt = 0;
+    // The kernel arguments are read through a pointer the compiler cannot see
+    // across tasks (a is the kernel's only argument: it sits at the start of the
+    // kernel-argument segment), so that they are loaded inside each task, as a
+    // kernel of one task would: hoisted out of the loop they would all stay live
+    // around it and push the registers of the gather and MFMA loop into scratch.
+    typedef const __attribute__((address_space(4))) DecodeArgs* KernargPtr;
+    KernargPtr ap = (KernargPtr)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(ap));
+    const int grp = task - (task / G) * G;
+    LDS_PTR(int32_t) slot = (LDS_PTR(int32_t))(lds + Cfg::kTaskSlotBase) + (k & 1);
+    decode_task<FP8, HW, KW, NS, WPE, KD, VD, QC, QF8>(*(const DecodeArgs*)ap, lds, b, chunk, grp, nxt);
+    if (wave == 0 && lane == 0) {
+      *slot = nxt;
+      if (nxt == W + n_tasks - 1)  // the call's last value: every workgroup has taken its last
+        __hip_atomic_store(a.status + 2, (uint32_t)W, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // every wave is done with the ring, the merge area and this task before the next task's
+    // loads land there, and the next task's index is in the slot
+    __syncthreads();
+    task = __builtin_amdgcn_readfirstlane(*slot);
+    if (task < n_tasks) {
+      const int item = task / G;
+      b = a.work[2 * item];
+      chunk = a.work[2 * item + 1];
+      asm volatile("" ::"s"(b), "s"(chunk));
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Combine: one workgroup (256 threads) per (column block of CB columns, tile
 // row, sequence x group), in a single pass over the partial records: the
@@ -1134,10 +1235,14 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
   __shared__ float m_lds[kStreams], s_lds[kStreams], w_lds[kStreams];
   __shared__ float total_lds;
   __shared__ __attribute__((aligned(16))) float acc_lds[kStreams][CB];
-  const int colblk = blockIdx.x;
-  const int rr = blockIdx.y;
-  const int b = blockIdx.z / a.num_groups;
-  const int grp = blockIdx.z % a.num_groups;
+  // blockIdx.x = (sequence x group, tile row, column block), column block fastest
+  constexpr int kColBlocks = kLatentDim / CB;
+  const int64_t t = blockIdx.x / kColBlocks;
+  const int colblk = (int)(blockIdx.x - t * kColBlocks);
+  const int rr = (int)(t % a.rows_per_group);
+  const int bg = (int)(t / a.rows_per_group);
+  const int b = bg / a.num_groups;
+  const int grp = bg % a.num_groups;
   const int n_b = a.nchunks[b];
   const int pbase = a.partbase[b];
   asm volatile("" ::"s"(n_b), "s"(pbase));  // one round trip for both
@@ -1213,11 +1318,65 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
   }
 }
 
-template <bool FP8, int HW, int KW, int NS, int WPE, int KD, int VD, int QC, bool QF8 = false>
-int launch_decode_t(const DecodeArgs& a, int gx, int gy, int gz, hipStream_t st) {
-  hipLaunchKernelGGL((mla_decode_kernel<FP8, HW, KW, NS, WPE, KD, VD, QC, QF8>), dim3(gx, gy, gz), dim3(HW * KW * 64), 0,
-                     st, a);
-  return (int)hipGetLastError();
+// One decode configuration: the template arguments of a kernel instance and
+// FIT, the workgroups of it that one CU holds, which the planner uses as the
+// occupancy of the persistent grid. FIT is checked against what the LDS
+// footprint and the waves (WPE per SIMD, four SIMDs) allow.
+template <bool FP8, int HW, int KW, int NS, int WPE, int KD, int VD, int QC, bool QF8, int FIT>
+struct DecodeConfig {
+  using Cfg = DecodeCfg<FP8, HW, KW, NS>;
+  static constexpr int kLdsPerCu = 160 * 1024;
+  static constexpr int kLdsFit = kLdsPerCu / Cfg::kLdsBytes;
+  static constexpr int kWaveFit = 4 * WPE / (HW * KW);
+  static_assert(FIT >= 1 && FIT == (kLdsFit < kWaveFit ? kLdsFit : kWaveFit),
+                "the stated workgroups per CU are what the LDS and the waves allow");
+  static constexpr int kFit = FIT;
+  static int launch(const DecodeArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL((mla_decode_kernel<FP8, HW, KW, NS, WPE, KD, VD, QC, QF8>), dim3(a.num_workgroups),
+                       dim3(HW * KW * 64), 0, st, a);
+    return (int)hipGetLastError();
+  }
+};
+
+struct NoConfig {};
+
+// The configuration of each (cache type, query type, tile class), for launches
+// and for the planner's occupancy alike. Tile classes (head tiles HW x row
+// slices KW, one wave per SIMD unless noted; stages = as many blocks as the LDS
+// holds):
+//   16 rows:  1 x 4 (fp8, 128-row blocks) or 1 x 2 (bf16, 64-row blocks)
+//   32 rows:  2 x 2 (64-row blocks)
+//   64 rows:  4 x 1 (fp8, 32-row blocks, two workgroups per CU) or 4 x 2 (bf16,
+//             64-row blocks); two waves per SIMD of 256 registers each
+//   128 rows: 8 x 1 (32-row blocks, two waves per SIMD, 256 registers each)
+// Score sums are split over 4 accumulator chains where registers allow. For
+// the two-waves-per-SIMD kernels, ring depths are the deepest that keep every
+// register out of scratch inside the loop (measured: a single spill costs more
+// than any ring depth gains). For fp8, KD counts 32-byte units (two reads).
+template <typename F>
+int dispatch_decode(int kv_dtype, bool q_fp8, int tile_class, F&& f) {
+  const bool fp8 = kv_dtype == MLA_KV_FP8_E4M3FN;
+  if (q_fp8) {  // fp8 query x fp8 cache: the fp8-cache configurations
+    if (!fp8) return f(NoConfig{});
+    switch (tile_class) {
+      case 0: return f(DecodeConfig<true, 1, 4, 2, 1, 4, 8, 4, true, 1>{});
+      case 1: return f(DecodeConfig<true, 2, 2, 4, 1, 4, 8, 4, true, 1>{});
+      case 2: return f(DecodeConfig<true, 4, 1, 4, 2, 3, 3, 1, true, 2>{});
+      case 3: return f(DecodeConfig<true, 8, 1, 8, 2, 3, 3, 1, true, 1>{});
+    }
+    return f(NoConfig{});
+  }
+  switch (tile_class) {
+    case 0: return fp8 ? f(DecodeConfig<true, 1, 4, 2, 1, 4, 8, 4, false, 1>{})
+                       : f(DecodeConfig<false, 1, 2, 2, 1, 8, 8, 4, false, 1>{});
+    case 1: return fp8 ? f(DecodeConfig<true, 2, 2, 4, 1, 4, 8, 4, false, 1>{})
+                       : f(DecodeConfig<false, 2, 2, 2, 1, 8, 8, 4, false, 1>{});
+    case 2: return fp8 ? f(DecodeConfig<true, 4, 1, 4, 2, 3, 3, 1, false, 2>{})
+                       : f(DecodeConfig<false, 4, 2, 2, 2, 3, 3, 2, false, 1>{});
+    case 3: return fp8 ? f(DecodeConfig<true, 8, 1, 8, 2, 3, 3, 1, false, 1>{})
+                       : f(DecodeConfig<false, 8, 1, 4, 2, 4, 3, 1, false, 1>{});
+  }
+  return f(NoConfig{});
 }
 
 }  // namespace
@@ -1227,49 +1386,29 @@ int launch_plan(const PlanArgs& a, void* stream) {
   return (int)hipGetLastError();
 }
 
-// Tile classes (head tiles HW x row slices KW, one wave per SIMD unless
-// noted; stages = as many blocks as the LDS holds):
-//   16 rows:  1 x 4 (fp8, 128-row blocks) or 1 x 2 (bf16, 64-row blocks)
-//   32 rows:  2 x 2 (64-row blocks)
-//   64 rows:  4 x 2 (64-row blocks, two waves per SIMD, 256 registers each)
-//   128 rows: 8 x 1 (32-row blocks, two waves per SIMD, 256 registers each)
-// Score sums are split over 4 accumulator chains where registers allow. For
-// the two-waves-per-SIMD kernels, ring depths are the deepest that keep every
-// register out of scratch inside the loop (measured: a single spill costs more
-// than any ring depth gains). For fp8, KD counts 32-byte units (two reads).
-int launch_decode(const DecodeArgs& a, int kv_dtype, bool q_fp8, int tile_class, int gx, int gy, int gz,
-                  void* stream) {
-  hipStream_t st = (hipStream_t)stream;
-  const bool fp8 = kv_dtype == MLA_KV_FP8_E4M3FN;
-  if (q_fp8) {  // fp8 query x fp8 cache: the fp8-cache configurations
-    if (!fp8) return (int)hipErrorInvalidValue;
-    switch (tile_class) {
-      case 0: return launch_decode_t<true, 1, 4, 2, 1, 4, 8, 4, true>(a, gx, gy, gz, st);
-      case 1: return launch_decode_t<true, 2, 2, 4, 1, 4, 8, 4, true>(a, gx, gy, gz, st);
-      case 2: return launch_decode_t<true, 4, 1, 4, 2, 3, 3, 1, true>(a, gx, gy, gz, st);
-      case 3: return launch_decode_t<true, 8, 1, 8, 2, 3, 3, 1, true>(a, gx, gy, gz, st);
+int decode_wg_per_cu_fit(int kv_dtype, bool q_fp8, int tile_class) {
+  return dispatch_decode(kv_dtype, q_fp8, tile_class, [](auto c) -> int {
+    if constexpr (std::is_same_v<decltype(c), NoConfig>) {
+      return 1;
+    } else {
+      return decltype(c)::kFit;
     }
-    return (int)hipErrorInvalidValue;
-  }
-  switch (tile_class) {
-    case 0: return fp8 ? launch_decode_t<true, 1, 4, 2, 1, 4, 8, 4>(a, gx, gy, gz, st)
-                       : launch_decode_t<false, 1, 2, 2, 1, 8, 8, 4>(a, gx, gy, gz, st);
-    case 1: return fp8 ? launch_decode_t<true, 2, 2, 4, 1, 4, 8, 4>(a, gx, gy, gz, st)
-                       : launch_decode_t<false, 2, 2, 2, 1, 8, 8, 4>(a, gx, gy, gz, st);
-    case 2: return fp8 ? launch_decode_t<true, 4, 1, 4, 2, 3, 3, 1>(a, gx, gy, gz, st)
-                       : launch_decode_t<false, 4, 2, 2, 2, 3, 3, 2>(a, gx, gy, gz, st);
-    case 3: return fp8 ? launch_decode_t<true, 8, 1, 8, 2, 3, 3, 1>(a, gx, gy, gz, st)
-                       : launch_decode_t<false, 8, 1, 4, 2, 4, 3, 1>(a, gx, gy, gz, st);
-  }
-  return (int)hipErrorInvalidValue;
+  });
 }
 
+int launch_decode(const DecodeArgs& a, int kv_dtype, bool q_fp8, int tile_class, void* stream) {
+  return dispatch_decode(kv_dtype, q_fp8, tile_class, [&](auto c) -> int {
+    if constexpr (std::is_same_v<decltype(c), NoConfig>) {
+      return (int)hipErrorInvalidValue;
+    } else {
+      return decltype(c)::launch(a, (hipStream_t)stream);
+    }
+  });
+}
 
 int launch_combine(const CombineArgs& a, int max_chunks, void* stream) {
   hipStream_t st = (hipStream_t)stream;
-  const int rows = a.rows_per_group;
-  const int gz = a.batch * a.num_groups;
-  const int64_t row_count = (int64_t)gz * rows;
+  const int64_t row_count = (int64_t)a.batch * a.num_groups * a.rows_per_group;
   if (max_chunks <= 16) {
     const int64_t wgs = (row_count + 3) / 4;
     if (wgs > 0x7fffffff) return (int)hipErrorInvalidValue;
@@ -1279,13 +1418,17 @@ int launch_combine(const CombineArgs& a, int max_chunks, void* stream) {
       hipLaunchKernelGGL(mla_combine_rows_kernel<16>, dim3((unsigned)wgs), dim3(256), 0, st, a);
     return (int)hipGetLastError();
   }
-  // Narrow column blocks when few rows carry long chunk lists.
-  if (row_count >= 1024) {
-    hipLaunchKernelGGL(mla_combine_kernel<512>, dim3(1, rows, gz), dim3(256), 0, st, a);
-  } else if (row_count >= 128) {
-    hipLaunchKernelGGL(mla_combine_kernel<128>, dim3(kLatentDim / 128, rows, gz), dim3(256), 0, st, a);
+  // Narrow column blocks when few rows carry long chunk lists; one grid dimension of
+  // (rows x column blocks) workgroups.
+  const int cb = row_count >= 1024 ? 512 : row_count >= 128 ? 128 : 16;
+  const int64_t wgs = row_count * (kLatentDim / cb);
+  if (wgs > 0x7fffffff) return (int)hipErrorInvalidValue;
+  if (cb == 512) {
+    hipLaunchKernelGGL(mla_combine_kernel<512>, dim3((unsigned)wgs), dim3(256), 0, st, a);
+  } else if (cb == 128) {
+    hipLaunchKernelGGL(mla_combine_kernel<128>, dim3((unsigned)wgs), dim3(256), 0, st, a);
   } else {
-    hipLaunchKernelGGL(mla_combine_kernel<16>, dim3(kLatentDim / 16, rows, gz), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(mla_combine_kernel<16>, dim3((unsigned)wgs), dim3(256), 0, st, a);
   }
   return (int)hipGetLastError();
 }

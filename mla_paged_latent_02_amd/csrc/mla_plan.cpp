@@ -1,12 +1,13 @@
-// Host half of the work planner: argument validation, the chunk rule and the
-// workspace layout. Pure integer arithmetic, no device work.
+// Host half of the work planner: argument validation, the persistent grid, the
+// chunk rule and the workspace layout. Pure integer arithmetic, no device work.
 //
-// Rule sources: "perf(mla): chunk the non-FP4 gather_kv_b_proj over KV"
-// (description: one program per (batch, head, KV chunk), grid sized from the
-// longest sequence, early exit past a sequence's chunk count, and 12 programs
-// on 256 CUs starving HBM) and "HK MLA: MI35x m16x8 retune, new m16x4 kernel,
-// page_size + mask support" (Summary: heads x query tokens stacked into 64- or
-// 128-row tiles; metadata sized for num_cu clusters, doubled at occupancy 2).
+// Rule sources: "HK MLA: MI35x m16x8 retune, new m16x4 kernel, page_size +
+// mask support" (Summary and file table: a persistent decode kernel whose
+// device-built metadata is sized for num_cu clusters, doubled when the 64-row
+// kernel runs at occupancy 2; heads x query tokens stacked into 64- or 128-row
+// tiles) and "perf(mla): chunk the non-FP4 gather_kv_b_proj over KV"
+// (description: a long context split over KV chunks so that the whole device
+// streams; 12 programs on 256 CUs starve HBM).
 #include <cmath>
 #include <cstring>
 
@@ -44,7 +45,6 @@ mla_status_t validate_params(const mla_decode_params_t& p) {
   if (!std::isfinite(p.q_scale) || !(p.q_scale > 0.0f)) return MLA_ERR_INVALID_ARG;
   if (p.q_dtype == MLA_Q_BF16 && p.q_scale != 1.0f) return MLA_ERR_INVALID_ARG;
   if (p.q_dtype == MLA_Q_FP8_E4M3FN && p.kv_dtype != MLA_KV_FP8_E4M3FN) return MLA_ERR_UNSUPPORTED;
-  if (p.batch > 65535) return MLA_ERR_UNSUPPORTED;  // grid z limit
   return MLA_OK;
 }
 
@@ -97,7 +97,7 @@ mla_status_t mla_decode_plan_host(const mla_decode_params_t* params, const mla_p
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return MLA_ERR_HIP;
     num_cu = n;
   }
-  if (num_cu <= 0) return MLA_ERR_HIP;
+  if (num_cu <= 0 || num_cu > 65536) return MLA_ERR_UNSUPPORTED;
 
   const mla_decode_params_t& p = *params;
   const int64_t B = p.batch, S = p.seqlen_qo, H = p.num_heads, L = p.max_context_len;
@@ -110,23 +110,25 @@ mla_status_t mla_decode_plan_host(const mla_decode_params_t* params, const mla_p
     TR *= 2;
     ++cls;
   }
+  // the persistent grid: the requested workgroups per CU, capped at what the class's decode
+  // kernel holds (its LDS and waves)
+  const int32_t fit = mla::decode_wg_per_cu_fit(p.kv_dtype, p.q_dtype == MLA_Q_FP8_E4M3FN, cls);
+  const int64_t occ = opt.wg_per_cu[cls] < fit ? opt.wg_per_cu[cls] : fit;
+  const int64_t W = int64_t(num_cu) * occ;
   int64_t C;
   if (opt.force_chunk) {
     C = opt.force_chunk;
   } else {
-    // the target is capped at the workgroups the class's decode kernel fits per CU
-    // (its LDS footprint): only the fp8 64-row kernel holds two
-    static const int32_t kFit[2][4] = {{1, 1, 1, 1}, {1, 1, 2, 1}};  // [bf16, fp8][class]
-    const int32_t fit = kFit[p.kv_dtype == MLA_KV_FP8_E4M3FN ? 1 : 0][cls];
-    const int64_t wg = opt.wg_per_cu[cls] < fit ? opt.wg_per_cu[cls] : fit;
-    int64_t want = int64_t(num_cu) * wg / (B * G);
+    int64_t want = W / (B * G);
     if (want < 1) want = 1;
     C = cdiv(cdiv(L, want), mla::kBlockRows) * mla::kBlockRows;
     if (C < opt.chunk_min[cls]) C = opt.chunk_min[cls];
     if (C > opt.chunk_max[cls]) C = opt.chunk_max[cls];
   }
   const int64_t max_chunks = cdiv(L, C);
-  if (G > 65535 || max_chunks > 0x7fffffff || B * max_chunks * G > 0x7fffffff) return MLA_ERR_UNSUPPORTED;
+  // The device counts tasks (items x groups) and partial rows in 32 bits.
+  if (B * max_chunks * G > 0x7fffffff || B * G * max_chunks * rows > 0x7fffffff || W > 0x7fffffff)
+    return MLA_ERR_UNSUPPORTED;
 
   mla_plan_t plan;
   std::memset(&plan, 0, sizeof(plan));
@@ -141,10 +143,9 @@ mla_status_t mla_decode_plan_host(const mla_decode_params_t* params, const mla_p
   plan.tile_class = cls;
   plan.chunk_len = int32_t(C);
   plan.max_chunks = int32_t(max_chunks);
+  plan.wg_per_cu = int32_t(occ);
+  plan.num_workgroups = int32_t(W);
   plan.work_capacity = B * max_chunks;
-  plan.grid[0] = int32_t(plan.work_capacity * G);
-  plan.grid[1] = 1;
-  plan.grid[2] = 1;
   plan.partial_capacity_records = B * G * max_chunks;
   uint64_t off = 0;
   plan.ws_status_offset = off;

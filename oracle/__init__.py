@@ -56,7 +56,7 @@ from .attention import (
     mla_decode_reference,
     mla_decode_reference_one,
 )
-from .planner import PlanOptions, reference_plan, device_plan_arrays, work_list
+from .planner import PlanOptions, reference_plan, device_plan_arrays, work_list, status_words, first_task
 from .insert import bf16_bits_to_f32, f32_to_bf16_rne, f32_to_e4m3fn, rope_f32, qcat_cache_insert_reference
 from .kv_b_proj import gather_kv_b_proj_reference, output_rows, rope_bits
 
@@ -78,6 +78,8 @@ __all__ = [
     "reference_plan",
     "device_plan_arrays",
     "work_list",
+    "status_words",
+    "first_task",
     "bf16_bits_to_f32",
     "f32_to_bf16_rne",
     "f32_to_e4m3fn",

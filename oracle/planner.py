@@ -1,20 +1,22 @@
 """Reference work planner for split-KV MLA decode (test infrastructure).
 
 An independent Python statement of the plan rule, used to check the library's
-host planner (plan fields) and device planner (per-sequence arrays) bit for bit.
-It shares no code with the library.
+host planner (plan fields) and device planner (per-sequence arrays, status
+words and the work list) bit for bit. It shares no code with the library;
+nothing in the library imports it.
 
 Where the rule comes from:
 
 * "perf(mla): chunk the non-FP4 gather_kv_b_proj over KV" (description): the
-  serial walk over the context becomes a grid axis of KV chunks; the grid is
-  sized from the longest sequence and a program whose chunk index is at or past
-  its own sequence's chunk count returns at once, so ragged batches stay correct.
-  Too few programs starve HBM (12 workgroups on a 256-CU part).
+  serial walk over the context becomes a set of KV chunks sized from the
+  longest sequence; no program works past its own sequence's end, so ragged
+  batches stay correct. Too few programs starve HBM (12 workgroups on a 256-CU
+  part).
 * "HK MLA: MI35x m16x8 retune, new m16x4 kernel, page_size + mask support"
-  (Summary): heads times query tokens are stacked into one tile of rows
-  (num_heads * max_seqlen_qo of 64 or 128); metadata is sized for ``num_cu``
-  clusters, or twice that when the 64-row kernel runs at occupancy 2.
+  (Summary and file table): the decode kernel is persistent; device-built
+  metadata sizes its grid for ``num_cu`` clusters, or twice that when the
+  64-row kernel runs at occupancy 2; heads times query tokens are stacked into
+  one tile of rows (64 or 128).
 
 The rule (all integer arithmetic):
 
@@ -22,12 +24,14 @@ The rule (all integer arithmetic):
     G    = ceil(H / hpg)               head groups
     rows = hpg * S                     valid rows of a tile
     TR   = 16 | 32 | 64 | 128          smallest of these >= rows; class = log2(TR/16)
+    occ  = min(wg_per_cu[cls], fit[kv_dtype][cls])
+           (fit: workgroups of that class's decode kernel one CU holds)
+    W    = num_cu * occ                persistent workgroups: the decode grid
     C    = force_chunk if set, else
            clamp(roundup(ceil(Lmax / want), 64), chunk_min[cls], chunk_max[cls])
-           with want = max(1, floor(num_cu * min(wg_per_cu[cls], fit[kv_dtype][cls]) / (B * G)))
-           (fit: workgroups the decode kernel of that cache type and class holds per CU)
+           with want = max(1, floor(W / (B * G)))
     max_chunks = ceil(Lmax / C)
-    work_capacity = B * max_chunks     decode grid = (work_capacity * G, 1, 1)
+    work_capacity = B * max_chunks     entries of the work list
 
 Per sequence (device half): a sequence is valid when ``S <= ctx_b <= Lmax`` and
 its page list holds at least ``ceil(ctx_b / P)`` pages; then
@@ -36,14 +40,22 @@ its page list holds at least ``ceil(ctx_b / P)`` pages; then
 ``(n_b if n_b > 1 else 0) * G``: partial records of sequence b, group g, chunk c
 sit at record ``part_base_b + g * n_b + c``.
 
-Work list (dispatch order; a design choice of this library, not from the
-pages): workgroups run longest work first so that the last workgroups on the
-CUs are short. Items are (sequence, chunk): every full chunk (exactly C rows)
-in (sequence, chunk) order; then each sequence's partial last chunk (length
-r = ctx - (n - 1) * C < C), by length class floor(16 * r / C) from the
-longest class down, ties by sequence; then one item (sequence, -1) per invalid
-sequence, whose rows are filled with NaN. Workgroup x of the decode grid runs
-item x // G for head group x % G.
+Work list (a design choice of this library, not from the pages): items
+(sequence, chunk), longest work first so that the last tasks a workgroup takes
+are short. Every full chunk (exactly C rows) in (sequence, chunk) order; then
+each sequence's partial last chunk (length r = ctx - (n - 1) * C < C), by length
+class floor(16 * r / C) from the longest class down, ties by sequence; then one
+item (sequence, -1) per invalid sequence, whose rows are filled with NaN.
+
+Tasks and workgroups: task t is item t // G for head group t % G. Workgroup x
+of the persistent grid first runs task first_task(x, W) (consecutive tasks on
+one XCD: the hardware deals workgroups to the 8 XCDs in turn, so the groups
+and chunks of one sequence share an L2), then takes the next untaken task from
+a counter, in list order, as each task's last block starts, until none is
+left: so a workgroup takes more work when it is about to be free, in
+longest-first order, whatever the order in which the hardware starts
+workgroups. Status words after the plan (and after every decode call): (OR of
+the status bits, item count, W = the counter's start, 0).
 """
 
 from dataclasses import dataclass, field
@@ -66,6 +78,7 @@ def _cdiv(a: int, b: int) -> int:
 # workgroups per CU that the decode kernel of each cache type and tile class fits
 # (its LDS footprint); the target wg_per_cu is capped at it
 KERNEL_WG_PER_CU = {"bf16": [1, 1, 1, 1], "fp8_e4m3fn": [1, 1, 2, 1]}
+NUM_XCD = 8
 
 
 @dataclass
@@ -86,11 +99,12 @@ def reference_plan(batch, seqlen_qo, num_heads, max_context_len, num_cu, options
     rows = hpg * S
     TR = next(t for t in TILE_CLASSES if t >= rows)
     cls = TILE_CLASSES.index(TR)
+    occ = min(o.wg_per_cu[cls], KERNEL_WG_PER_CU[kv_dtype][cls])
+    W = int(num_cu) * occ
     if o.force_chunk:
         C = int(o.force_chunk)
     else:
-        wg = min(o.wg_per_cu[cls], KERNEL_WG_PER_CU[kv_dtype][cls])
-        want = max(1, (num_cu * wg) // (B * G))
+        want = max(1, W // (B * G))
         C = _cdiv(_cdiv(L, want), BLOCK_ROWS) * BLOCK_ROWS
         C = min(max(C, o.chunk_min[cls]), o.chunk_max[cls])
     max_chunks = _cdiv(L, C)
@@ -103,7 +117,9 @@ def reference_plan(batch, seqlen_qo, num_heads, max_context_len, num_cu, options
         "tile_class": cls,
         "chunk_len": C,
         "max_chunks": max_chunks,
-        "grid": (B * max_chunks * G, 1, 1),
+        "wg_per_cu": occ,
+        "num_workgroups": W,
+        "grid": (W, 1, 1),
         "partial_capacity_records": B * G * max_chunks,
     }
 
@@ -149,3 +165,16 @@ def work_list(plan, n_chunks, context_lens):
             partial.append((LENGTH_CLASSES * last // C, b, n - 1))
     partial.sort(key=lambda t: (-t[0], t[1]))
     return full + [(b, c) for _, b, c in partial] + invalid
+
+
+def status_words(plan, status_bits, n_items):
+    """The four status words the planner writes (and every decode call leaves behind)."""
+    return [int(status_bits), int(n_items), plan["num_workgroups"], 0]
+
+
+def first_task(x, num_workgroups):
+    """The task workgroup x of the persistent grid runs first (a permutation of [0, W))."""
+    W = int(num_workgroups)
+    if W % NUM_XCD:
+        return x
+    return (x % NUM_XCD) * (W // NUM_XCD) + x // NUM_XCD

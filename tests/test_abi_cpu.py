@@ -83,7 +83,7 @@ def test_host_plan_matches_reference_planner_bit_exactly(shape, force, dt):
     ref = reference_plan(B, S, H, L, 256, RefOptions(force_chunk=force), kv_dtype=dt)
     got = mla.plan_to_dict(plan)
     assert got == {k: ref[k] for k in got}
-    assert plan.magic == 0x4D4C4131
+    assert plan.magic == 0x4D4C4132
     # workspace layout: 256-aligned, disjoint, in order, large enough for every partial
     offs = [plan.ws_status_offset, plan.ws_nchunks_offset, plan.ws_partbase_offset, plan.ws_part_out_offset,
             plan.ws_part_lse_offset, plan.ws_work_offset, plan.ws_bytes]
@@ -127,12 +127,34 @@ def test_non_default_options_follow_the_rule():
         assert got == {k: ref[k] for k in got}
 
 
+def test_large_batches_plan():
+    # no grid limit of 65535 applies: the decode grid is the persistent workgroups and the merge
+    # grids are one-dimensional
+    for B in (65535, 65536, 200000):
+        plan = mla.plan_host(params(batch=B, max_context_len=64, num_slots=16 * 4 * B), None, 256)
+        assert plan.num_workgroups == 256 and plan.work_capacity == B
+    # past the 32-bit task count: rejected as unsupported, before any device work
+    with pytest.raises(mla.MlaError) as e:
+        mla.plan_host(params(batch=2 ** 20, num_heads=2048, max_context_len=2 ** 20, num_slots=16), None, 256)
+    assert e.value.status == 2
+
+
+def test_persistent_grid_follows_the_kernel_occupancy():
+    # W = num_cu x min(requested workgroups per CU, what the class's kernel holds): the fp8 64-row
+    # kernel holds two per CU, every other one
+    for dt, S, H, want in (("fp8_e4m3fn", 4, 16, 2), ("bf16", 4, 16, 1), ("fp8_e4m3fn", 1, 128, 1),
+                           ("fp8_e4m3fn", 1, 12, 1), ("bf16", 1, 128, 1)):
+        kw = dict(kv_dtype=dt, kv_scale=1.0 if dt == "bf16" else 0.01, seqlen_qo=S, num_heads=H)
+        plan = mla.plan_host(params(**kw), mla.make_options(wg_per_cu=[4, 4, 4, 4]), 100)
+        assert (plan.wg_per_cu, plan.num_workgroups) == (want, 100 * want), (dt, S, H)
+
+
 @pytest.mark.parametrize("bad, code", [
     (dict(batch=0), 1), (dict(seqlen_qo=0), 1), (dict(seqlen_qo=9), 2), (dict(num_heads=0), 1),
     (dict(page_size=0), 1), (dict(max_context_len=0), 1), (dict(causal=2), 1), (dict(kv_dtype=7), 1),
     (dict(softmax_scale=float("nan")), 1), (dict(softmax_scale=0.0), 1), (dict(kv_scale=0.0), 1),
     (dict(kv_scale=-1.0), 1), (dict(kv_dtype="bf16", kv_scale=0.5), 1), (dict(num_slots=0), 1),
-    (dict(num_slots=4097), 1), (dict(batch=70000), 2), (dict(seqlen_qo=4, max_context_len=3), 1),
+    (dict(num_slots=4097), 1), (dict(seqlen_qo=4, max_context_len=3), 1),
     (dict(q_dtype=2), 1), (dict(q_dtype="fp8_e4m3fn", q_scale=0.0), 1),
     (dict(q_dtype="fp8_e4m3fn", q_scale=float("inf")), 1), (dict(q_scale=0.5), 1),
     (dict(q_dtype="fp8_e4m3fn", q_scale=0.5, kv_dtype="bf16", kv_scale=1.0), 2),

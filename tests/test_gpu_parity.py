@@ -41,10 +41,10 @@ def upload(case):
         q_dtype=case.q_dtype, q_scale=case.q_scale)
 
 
-def run(case, options=None, inputs=None):
+def run(case, options=None, inputs=None, num_cu=0):
     from mla_paged_latent_02_amd.device import Decoder
     inp = inputs or upload(case)
-    dec = Decoder(inp, options, poison=True)
+    dec = Decoder(inp, options, num_cu=num_cu, poison=True)
     out, lse = dec()
     torch.cuda.synchronize()
     return dec, out.float().cpu().numpy(), lse.cpu().numpy()
@@ -70,16 +70,21 @@ def assert_close(case, out, lse, batches=None, label=""):
 
 
 def check_plan_arrays(case, dec):
+    """Plan fields, per-sequence arrays, status words and the work list equal the oracle planner's,
+    bit for bit, after the decode call too: the task counter is back at its start. Returns the
+    status bits."""
     import mla_paged_latent_02_amd as mla
     n, base, status = mla.read_plan_arrays(dec.plan, dec.workspace)
     ref = oracle.reference_plan(case.batch, case.seqlen_qo, case.num_heads, case.max_context_len,
                                 dec.plan.num_cu, _ref_options(dec.plan), kv_dtype=case.kv_dtype)
     assert mla.plan_to_dict(dec.plan) == {k: ref[k] for k in mla.plan_to_dict(dec.plan)}
-    rn, rbase, rstatus = oracle.device_plan_arrays(ref, case.seqlen_qo, case.max_context_len, case.page_size,
-                                                   case.context_lens, case.kv_indptr)
-    assert n == rn and base == rbase and status == rstatus
-    assert mla.read_work_list(dec.plan, dec.workspace) == oracle.work_list(ref, rn, case.context_lens)
-    return status
+    rn, rbase, rbits = oracle.device_plan_arrays(ref, case.seqlen_qo, case.max_context_len, case.page_size,
+                                                 case.context_lens, case.kv_indptr)
+    items = oracle.work_list(ref, rn, case.context_lens)
+    assert n == rn and base == rbase
+    assert status == oracle.status_words(ref, rbits, len(items))
+    assert mla.read_work_list(dec.plan, dec.workspace) == items
+    return status[0]
 
 
 def _ref_options(plan):
@@ -90,6 +95,12 @@ def _ref_options(plan):
 def options(force_chunk=0):
     import mla_paged_latent_02_amd as mla
     return mla.make_options(force_chunk=force_chunk)
+
+
+# (forced chunk length, num_cu) of the grid tests: the default plan on the device's CUs; a
+# forced chunk length on the device's CUs; the forced length on three CUs, so that a few
+# persistent workgroups each take many tasks from the counter.
+SPLITS = [(0, 0), (128, 0), (128, 3)]
 
 
 # ------------------------------------------------------------------ small cases, full comparison
@@ -106,8 +117,8 @@ def test_tiny_workload_forced_split_exercises_the_combine():
     case = make_case(**WORKLOADS["tiny_b2_h16"])
     dec, out, lse = run(case, options(force_chunk=64))
     check_plan_arrays(case, dec)
-    n, _, _ = __import__("mla_paged_latent_02_amd").read_plan_arrays(dec.plan, dec.workspace)
-    assert n == [1, 2]
+    n, _, status = __import__("mla_paged_latent_02_amd").read_plan_arrays(dec.plan, dec.workspace)
+    assert n == [1, 2] and status[1] == 3
     assert_close(case, out, lse, label="tiny split")
 
 
@@ -127,10 +138,10 @@ def test_boundary_grid(kv_dtype, S, H, causal, P):
     seed = 1000 + GRID.index((kv_dtype, S, H, causal, P))
     case = make_case(batch=len(ctx), seqlen_qo=S, num_heads=H, ctx=ctx, page_size=P, kv_dtype=kv_dtype,
                      causal=causal, seed=seed, pool_pages=sum(-(-c // P) for c in ctx) + 3)
-    for force in (0, C):
-        dec, out, lse = run(case, options(force_chunk=force))
+    for force, num_cu in SPLITS:
+        dec, out, lse = run(case, options(force_chunk=force), num_cu=num_cu)
         check_plan_arrays(case, dec)
-        assert_close(case, out, lse, label=f"grid force={force}")
+        assert_close(case, out, lse, label=f"grid force={force} num_cu={num_cu}")
 
 
 # fp8 query x fp8 cache: every tile class, page size and causal shape of the grid above
@@ -145,10 +156,10 @@ def test_boundary_grid_fp8_query(S, H, causal, P):
     case = make_case(batch=len(ctx), seqlen_qo=S, num_heads=H, ctx=ctx, page_size=P, kv_dtype="fp8_e4m3fn",
                      causal=causal, seed=seed, pool_pages=sum(-(-c // P) for c in ctx) + 3, q_dtype="fp8_e4m3fn")
     assert case.q_bits.dtype == np.uint8
-    for force in (0, C):
-        dec, out, lse = run(case, options(force_chunk=force))
+    for force, num_cu in SPLITS:
+        dec, out, lse = run(case, options(force_chunk=force), num_cu=num_cu)
         check_plan_arrays(case, dec)
-        assert_close(case, out, lse, label=f"fp8 query grid force={force}")
+        assert_close(case, out, lse, label=f"fp8 query grid force={force} num_cu={num_cu}")
 
 
 # shapes the grid does not reach: the largest seqlen_qo (8), one head, 256 heads (two head
@@ -170,10 +181,10 @@ def test_edge_shapes(q_dtype, kv_dtype, S, H, causal, P, ctx):
         (2 if q_dtype != "bf16" else 0)
     case = make_case(batch=len(ctx), seqlen_qo=S, num_heads=H, ctx=ctx, page_size=P, kv_dtype=kv_dtype,
                      causal=causal, seed=seed, pool_pages=sum(-(-c // P) for c in ctx) + 2, q_dtype=q_dtype)
-    for force in (0, 64):
-        dec, out, lse = run(case, options(force_chunk=force))
+    for force, num_cu in ((0, 0), (64, 0), (64, 2)):
+        dec, out, lse = run(case, options(force_chunk=force), num_cu=num_cu)
         check_plan_arrays(case, dec)
-        assert_close(case, out, lse, label=f"edge S={S} H={H} P={P} force={force}")
+        assert_close(case, out, lse, label=f"edge S={S} H={H} P={P} force={force} num_cu={num_cu}")
 
 
 # merge paths: at most 16 chunks -> one wave per row; more -> column blocks of 16, 128 or 512
@@ -192,6 +203,53 @@ def test_merge_paths(batch, heads, ctx, expect_many):
     check_plan_arrays(case, dec)
     assert (dec.plan.max_chunks > 16) == expect_many
     assert_close(case, out, lse, label=f"merge B={batch} H={heads}")
+
+
+def test_one_cu_runs_the_whole_batch():
+    # num_cu = 1: the two persistent workgroups of one CU (64-row tiles at occupancy 2) take
+    # all of the batch's 43 tasks (chunks of 64 rows) from the counter in turn
+    case = make_case(batch=6, seqlen_qo=4, num_heads=16, ctx=[4, 700, 65, 1300, 17, 400], page_size=16,
+                     kv_dtype="fp8_e4m3fn", causal=True, seed=84)
+    dec, out, lse = run(case, options(force_chunk=64), num_cu=1)
+    assert dec.plan.num_workgroups == 2
+    check_plan_arrays(case, dec)
+    assert_close(case, out, lse, label="one CU")
+
+
+def test_counters_are_reset_after_every_call():
+    # the last workgroup to finish sets the task counter back, so that call after call (on
+    # one plan, on the same workspace) starts from the same state
+    import mla_paged_latent_02_amd as mla
+    case = make_case(batch=9, seqlen_qo=1, num_heads=128, ctx=[1100, 64, 700, 1, 900, 130, 1000, 65, 1024],
+                     page_size=16, kv_dtype="bf16", seed=86)
+    dec, out, lse = run(case, options(force_chunk=64), num_cu=5)
+    bits = check_plan_arrays(case, dec)
+    for _ in range(3):
+        o2, l2 = dec()
+        torch.cuda.synchronize()
+        _, _, status = mla.read_plan_arrays(dec.plan, dec.workspace)
+        assert status[0] == bits and status[2:] == [dec.plan.num_workgroups, 0]
+        assert np.array_equal(o2.float().cpu().numpy().view(np.uint32), out.view(np.uint32))
+
+
+def test_stale_plan_is_flagged():
+    # planned for one set of lengths, decoded with one sequence grown past its planned chunk
+    # count (a decode step without re-planning): the status bit is set. A sequence that grows
+    # within its chunk count is decoded in full and raises nothing.
+    import mla_paged_latent_02_amd as mla
+    case = make_case(batch=3, seqlen_qo=1, num_heads=16, ctx=[300, 128, 500], page_size=16, kv_dtype="bf16",
+                     seed=85, pool_pages=64)
+    dec, out, lse = run(case, options(force_chunk=128))
+    assert check_plan_arrays(case, dec) == 0
+    inp = dec.inputs
+    inp.context_lens[0] += 1  # 301 rows: still three chunks of 128
+    dec()
+    torch.cuda.synchronize()
+    assert mla.read_plan_arrays(dec.plan, dec.workspace)[2][0] == 0
+    inp.context_lens[1] += 1  # 129 rows: two chunks, one planned
+    dec()
+    torch.cuda.synchronize()
+    assert mla.read_plan_arrays(dec.plan, dec.workspace)[2][0] == mla.DEV_STALE_PLAN
 
 
 def test_run_to_run_bitwise_determinism():
@@ -232,7 +290,7 @@ def test_invalid_sequences_get_nan_rows_and_status_bits():
     dec, out, lse = run(case, options(force_chunk=64))
     check_plan_arrays(case, dec)
     n, _, status = mla.read_plan_arrays(dec.plan, dec.workspace)
-    assert status == (mla.DEV_CTX_TOO_SHORT | mla.DEV_CTX_TOO_LONG)
+    assert status[0] == (mla.DEV_CTX_TOO_SHORT | mla.DEV_CTX_TOO_LONG)
     assert n[1] == 0 and n[2] == 0
     assert np.isnan(out[1]).all() and np.isnan(out[2]).all()
     assert np.isnan(lse[1]).all() and np.isnan(lse[2]).all()
@@ -248,7 +306,7 @@ def test_short_page_list_and_bad_page_ids_are_flagged_not_read():
     case.kv_page_indices[case.kv_indptr[1]] = case.num_slots // 16 + 5
     dec, out, lse = run(case)
     _, _, status = mla.read_plan_arrays(dec.plan, dec.workspace)
-    assert status & mla.DEV_PAGE_OUT_OF_RANGE
+    assert status[0] & mla.DEV_PAGE_OUT_OF_RANGE
     case.kv_page_indices = good
     assert_close(case, out, lse, batches=[0, 2], label="bad page id in another sequence")
     # sequence 2: a page list one page short of its context length
@@ -257,7 +315,7 @@ def test_short_page_list_and_bad_page_ids_are_flagged_not_read():
     case2.kv_indptr[2] -= 1
     dec, out, lse = run(case2)
     n, _, status = mla.read_plan_arrays(dec.plan, dec.workspace)
-    assert status == mla.DEV_TOO_FEW_PAGES and n[1] == 0 and np.isnan(out[1]).all()
+    assert status[0] == mla.DEV_TOO_FEW_PAGES and n[1] == 0 and np.isnan(out[1]).all()
     assert_close(case2, out, lse, batches=[0], label="short page list next door")
 
 

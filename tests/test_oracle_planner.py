@@ -3,7 +3,7 @@
 import numpy as np
 import pytest
 
-from oracle import PlanOptions, reference_plan, device_plan_arrays, work_list
+from oracle import PlanOptions, reference_plan, device_plan_arrays, work_list, first_task
 from oracle.planner import STATUS_CTX_TOO_SHORT, STATUS_CTX_TOO_LONG, STATUS_TOO_FEW_PAGES
 
 
@@ -30,7 +30,7 @@ def test_plan_structure(shape):
     assert C % 64 == 0 and C >= 64
     assert p["max_chunks"] * C >= L and (p["max_chunks"] - 1) * C < L
     assert p["work_capacity"] == B * p["max_chunks"]
-    assert p["grid"] == (p["work_capacity"] * G, 1, 1)
+    assert p["num_workgroups"] == 256 * p["wg_per_cu"] and p["grid"] == (p["num_workgroups"], 1, 1)
 
 
 def test_plan_values_for_the_benchmark_shapes():
@@ -41,10 +41,11 @@ def test_plan_values_for_the_benchmark_shapes():
     # -> ceil(5200 / 4) = 1300 -> 1344 rows, 4 chunks
     p = reference_plan(128, 4, 16, 5200, 256, kv_dtype="fp8_e4m3fn")
     assert (p["heads_per_group"], p["tile_rows"], p["chunk_len"], p["max_chunks"]) == (16, 64, 1344, 4)
+    assert (p["wg_per_cu"], p["num_workgroups"]) == (2, 512)  # 512 chunks, one per persistent workgroup
     # the same shape with a bf16 cache: its 64-row kernel fits one workgroup per CU, so the target of 2
     # is capped at 1: want = 2 -> 2600 -> 2624 rows, 2 chunks
     p = reference_plan(128, 4, 16, 5200, 256, kv_dtype="bf16")
-    assert (p["chunk_len"], p["max_chunks"]) == (2624, 2)
+    assert (p["chunk_len"], p["max_chunks"], p["num_workgroups"]) == (2624, 2, 256)
     # small batches of 128 heads at ctx 8192: b = 1: want = 256 -> 32 -> 64 rows, raised to chunk_min = 128,
     # 64 chunks; b = 5: want = 51 -> 161 -> 192 rows, 43 chunks; b = 16: want = 16 -> 512 rows, 16 chunks
     for b, C, n in ((1, 128, 64), (5, 192, 43), (16, 512, 16)):
@@ -133,3 +134,49 @@ def test_work_list_covers_every_chunk_once_longest_first(seed):
         keys.append((-1 if r < 0 else 16 * r // C, b, c))
     assert all(keys[i][0] >= keys[i + 1][0] for i in range(len(keys) - 1))
     assert all(keys[i][1:] < keys[i + 1][1:] for i in range(len(keys) - 1) if keys[i][0] == keys[i + 1][0])
+
+
+def test_first_tasks_are_a_permutation_keeping_consecutive_tasks_on_one_xcd():
+    for W in (256, 512, 24, 7, 1):
+        ts = [first_task(x, W) for x in range(W)]
+        assert sorted(ts) == list(range(W))
+        if W % 8 == 0:
+            # workgroups x and x + 8 run on one XCD (the hardware deals them out in turn)
+            # and take consecutive tasks: the head groups and chunks of one sequence
+            assert all(ts[x + 8] == ts[x] + 1 for x in range(W - 8))
+
+
+def _simulate_counter(items_len, W, durations):
+    """Tasks handed out as the library's persistent workgroups take them: workgroup x first
+    runs first_task(x), then whichever workgroup frees up first takes the next task of the
+    list. Returns each workgroup's busy time."""
+    import heapq
+    busy = [0.0] * W
+    free = []
+    for x in range(W):
+        t = first_task(x, W)
+        if t < items_len:
+            busy[x] = durations[t]
+            heapq.heappush(free, (busy[x], x))
+    nxt = W
+    while nxt < items_len and free:
+        when, x = heapq.heappop(free)
+        busy[x] = when + durations[nxt]
+        heapq.heappush(free, (busy[x], x))
+        nxt += 1
+    return busy
+
+
+def test_longest_first_hand_out_balances_the_ragged_batch():
+    # the ragged 128-head batch (lengths as the benchmark draws them): with the list longest
+    # first and tasks handed out as workgroups free up, the busiest workgroup does at most 5%
+    # more rows than the mean
+    rng = np.random.default_rng([3, 3])
+    lens = rng.integers(21, 23333, size=256, endpoint=True)
+    plan = reference_plan(256, 1, 128, int(lens.max()), 256, kv_dtype="fp8_e4m3fn")
+    C = plan["chunk_len"]
+    n, _, _ = device_plan_arrays(plan, 1, int(lens.max()), 64, lens, np.concatenate([[0], np.cumsum(-(-lens // 64))]))
+    items = work_list(plan, n, lens)
+    rows = [min(C, int(lens[b]) - c * C) for b, c in items]
+    busy = _simulate_counter(len(items), plan["num_workgroups"], rows)
+    assert max(busy) <= 1.05 * sum(rows) / plan["num_workgroups"]
