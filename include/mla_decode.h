@@ -56,6 +56,7 @@ extern "C" {
 #define MLA_LATENT_DIM 512 /* V width = output width */
 #define MLA_MAX_SEQLEN_QO 8
 #define MLA_PLAN_MAGIC 0x4d4c4132u
+#define MLA_SCRATCH_BYTES (96u << 20) /* the static workspace of mla_decode_scratch, per device */
 
 typedef enum {
   MLA_OK = 0,
@@ -63,7 +64,8 @@ typedef enum {
   MLA_ERR_UNSUPPORTED = 2,         /* valid but outside the supported shapes */
   MLA_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes < plan->ws_bytes */
   MLA_ERR_HIP = 4,                 /* the HIP runtime reported an error */
-  MLA_ERR_BAD_PLAN = 5             /* plan not made by mla_decode_plan* */
+  MLA_ERR_BAD_PLAN = 5,            /* plan not made by mla_decode_plan* */
+  MLA_ERR_SCRATCH_TOO_SMALL = 6    /* mla_decode_scratch: the call needs more than MLA_SCRATCH_BYTES */
 } mla_status_t;
 
 typedef enum { MLA_KV_BF16 = 0, MLA_KV_FP8_E4M3FN = 1 } mla_kv_dtype_t;
@@ -251,6 +253,27 @@ mla_status_t mla_debug_read_plan_arrays(const mla_plan_t* plan, const void* d_wo
  */
 mla_status_t mla_debug_read_work_list(const mla_plan_t* plan, const void* d_workspace, int32_t* h_count,
                                       int32_t* h_items);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. The same work as
+ * mla_decode_plan + mla_decode + mla_split_combine on the caller's buffers, with
+ * the workspace in a static device array of MLA_SCRATCH_BYTES held by each
+ * device that loads the library until the process ends. Calls no hipMalloc,
+ * hipFree or allocating routine; the first call on a device looks up that
+ * device's array once. A call whose workspace (mla_decode_workspace_size) is
+ * larger than MLA_SCRATCH_BYTES returns MLA_ERR_SCRATCH_TOO_SMALL before any
+ * device work; use the workspace entry points for it. Every call on one device
+ * shares that device's array: the planner rewrites everything the decode reads,
+ * so nothing from an earlier call needs clearing, but calls that overlap on one
+ * device (unordered streams, or other host threads) race and must not be made.
+ * Arguments as for mla_decode_plan and mla_decode; out_plan (may be NULL)
+ * receives the plan, whose workspace offsets are into that array.
+ */
+mla_status_t mla_decode_scratch(const mla_decode_params_t* params, const mla_plan_options_t* options,
+                                int32_t num_cu, const void* d_q, const void* d_kv_cache, const int32_t* d_kv_indptr,
+                                const int32_t* d_kv_page_indices, const int32_t* d_context_lens, void* d_out,
+                                float* d_lse, void* stream, mla_plan_t* out_plan);
 
 /* ---- decode epilogue: query concat and latent-cache insert ---------------- */
 

@@ -30,7 +30,9 @@ _Q_DTYPES = {"bf16": 0, "fp8_e4m3fn": 1}  # mla_q_dtype_t
 
 MLA_OK = 0
 STATUS_NAMES = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED",
-                3: "MLA_ERR_WORKSPACE_TOO_SMALL", 4: "MLA_ERR_HIP", 5: "MLA_ERR_BAD_PLAN"}
+                3: "MLA_ERR_WORKSPACE_TOO_SMALL", 4: "MLA_ERR_HIP", 5: "MLA_ERR_BAD_PLAN",
+                6: "MLA_ERR_SCRATCH_TOO_SMALL"}
+SCRATCH_BYTES = 96 << 20  # MLA_SCRATCH_BYTES
 
 DEV_CTX_TOO_SHORT = 1
 DEV_CTX_TOO_LONG = 2
@@ -41,8 +43,8 @@ DEV_STALE_PLAN = 16
 # Every function the header declares, in declaration order.
 EXPORTED = ["mla_abi_version", "mla_status_string", "mla_plan_options_default", "mla_decode_plan_host",
             "mla_decode_workspace_size", "mla_decode_plan", "mla_decode", "mla_split_combine",
-            "mla_debug_read_plan_arrays", "mla_debug_read_work_list", "mla_qcat_cache_insert",
-            "mla_gather_kv_b_proj"]
+            "mla_debug_read_plan_arrays", "mla_debug_read_work_list", "mla_decode_scratch",
+            "mla_qcat_cache_insert", "mla_gather_kv_b_proj"]
 
 INSERT_SLOT_OUT_OF_RANGE = 1
 INSERT_POSITION_OUT_OF_RANGE = 2
@@ -108,6 +110,8 @@ def _load():
         "mla_split_combine": ([P(Plan), V, ctypes.c_size_t, V, V, V], ctypes.c_int),
         "mla_debug_read_plan_arrays": ([P(Plan), V, V, V, V], ctypes.c_int),
         "mla_debug_read_work_list": ([P(Plan), V, V, V], ctypes.c_int),
+        "mla_decode_scratch": ([P(DecodeParams), P(PlanOptions), ctypes.c_int32, V, V, V, V, V, V, V, V, P(Plan)],
+                               ctypes.c_int),
         "mla_qcat_cache_insert": ([P(InsertParams), V, V, V, V, V, V, V, V, V, V, V], ctypes.c_int),
         "mla_gather_kv_b_proj": ([P(KvbParams), V, V, V, V, V, V, V, V, V], ctypes.c_int),
     }
@@ -203,6 +207,18 @@ def decode(plan: Plan, q, kv_cache, kv_indptr, kv_page_indices, context_lens, ou
                          workspace.numel() * workspace.element_size(), _stream(stream))
     if st != MLA_OK:
         raise MlaError("mla_decode", st)
+
+
+def decode_scratch(params: DecodeParams, q, kv_cache, kv_indptr, kv_page_indices, context_lens, out, lse,
+                   options: Optional[PlanOptions] = None, num_cu: int = 0, stream=None) -> Plan:
+    """mla_decode_scratch: plan, decode and merge with the library's static workspace (no allocation)."""
+    plan = Plan()
+    st = _lib.mla_decode_scratch(ctypes.byref(params), ctypes.byref(options) if options else None, int(num_cu),
+                                 _ptr(q), _ptr(kv_cache), _ptr(kv_indptr), _ptr(kv_page_indices),
+                                 _ptr(context_lens), _ptr(out), _ptr(lse), _stream(stream), ctypes.byref(plan))
+    if st != MLA_OK:
+        raise MlaError("mla_decode_scratch", st)
+    return plan
 
 
 def split_combine(plan: Plan, workspace, out, lse, stream=None):

@@ -17,7 +17,7 @@ LIB_NAME = "libmla_decode.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["mla_kernels.hip", "mla_insert.hip", "mla_kv_b_proj.hip", "mla_api.cpp", "mla_plan.cpp"]
+SOURCES = ["mla_kernels.hip", "mla_insert.hip", "mla_kv_b_proj.hip", "mla_scratch.hip", "mla_api.cpp", "mla_plan.cpp"]
 
 # Packed fp32 ops are kept off in device code: hipcc -O3 would otherwise form
 # v_pk_{add,mul,fma}_f32 from plain float code.

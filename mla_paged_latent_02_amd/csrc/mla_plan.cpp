@@ -62,6 +62,7 @@ const char* mla_status_string(mla_status_t s) {
     case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case MLA_ERR_HIP: return "HIP runtime error";
     case MLA_ERR_BAD_PLAN: return "plan not made by mla_decode_plan";
+    case MLA_ERR_SCRATCH_TOO_SMALL: return "the call needs more workspace than the static scratch holds";
   }
   return "unknown status";
 }
