@@ -81,7 +81,7 @@ typedef enum { MLA_Q_BF16 = 0, MLA_Q_FP8_E4M3FN = 1 } mla_q_dtype_t;
 #define MLA_DEV_CTX_TOO_LONG 2u      /* context_lens[b] > max_context_len */
 #define MLA_DEV_TOO_FEW_PAGES 4u     /* page list shorter than ceil(ctx/page_size) */
 #define MLA_DEV_PAGE_OUT_OF_RANGE 8u /* a page index >= num_slots / page_size (or < 0) */
-#define MLA_DEV_STALE_PLAN 16u       /* mla_decode saw a context length of another chunk count than planned */
+#define MLA_DEV_STALE_PLAN 16u       /* mla_decode saw context lengths other than the planned ones */
 
 /* Shape and numeric parameters of one decode call. */
 typedef struct {
@@ -129,7 +129,8 @@ typedef struct {
   uint64_t ws_partbase_offset; /* int32 [B]: first partial record of each sequence */
   uint64_t ws_part_out_offset; /* float [records][rows_per_group][512]: normalised partial outputs */
   uint64_t ws_part_lse_offset; /* float [records][rows_per_group]: partial lse, base-2 log */
-  uint64_t ws_work_offset;     /* int32 [work_capacity][2]: (sequence, chunk) work items, longest first */
+  uint64_t ws_work_offset;     /* int32 [work_capacity][8]: work items, longest first: sequence, chunk, and the
+                                  sequence's planned ctx, page-list start, n_b and first record; 0, 0 */
   uint64_t ws_bytes;           /* total workspace bytes needed */
 } mla_plan_t;
 
@@ -188,9 +189,9 @@ size_t mla_decode_workspace_size(const mla_decode_params_t* params, const mla_pl
  * floor(16 r / C), longest class first, ties by b, then (b, -1) for every
  * invalid sequence; and the status words: the bits, the item count, the task
  * counter's start W and a reserved 0. d_context_lens [B] and
- * d_kv_indptr [B+1] are int32 device arrays. The plan stays valid for every
- * mla_decode / mla_split_combine call whose context lengths keep each
- * sequence's chunk count; mla_decode sets MLA_DEV_STALE_PLAN when one does not.
+ * d_kv_indptr [B+1] are int32 device arrays. The plan holds for the context
+ * lengths and page lists it was made with: mla_decode computes with the planned
+ * lengths and sets MLA_DEV_STALE_PLAN when d_context_lens differs from them.
  */
 mla_status_t mla_decode_plan(const mla_decode_params_t* params, const mla_plan_options_t* options,
                              int32_t num_cu, const int32_t* d_context_lens, const int32_t* d_kv_indptr,
@@ -215,7 +216,8 @@ mla_status_t mla_decode_plan(const mla_decode_params_t* params, const mla_plan_o
  *   d_kv_cache       [num_slots, 576] bf16 or fp8 e4m3fn bytes, contiguous
  *   d_kv_indptr      int32 [B+1]: page list of b is d_kv_page_indices[indptr[b] .. indptr[b+1])
  *   d_kv_page_indices int32 page ids (page p holds slots p*P .. p*P+P-1)
- *   d_context_lens   int32 [B]
+ *   d_context_lens   int32 [B]: compared with the planned lengths, which the call uses
+ *                    (MLA_DEV_STALE_PLAN when they differ)
  *   d_out            bf16 [B, S, H, 512]: written for sequences with n_b == 1;
  *                    sequences with n_b > 1 are written by mla_split_combine;
  *                    invalid sequences are filled with NaN
@@ -248,8 +250,8 @@ mla_status_t mla_debug_read_plan_arrays(const mla_plan_t* plan, const void* d_wo
 
 /*
  * Test hook: synchronously copies the work list to host memory. *h_count
- * receives the number of items; h_items (may be NULL) receives 2 * count
- * int32, (sequence, chunk) pairs, and must hold 2 * plan->work_capacity.
+ * receives the number of items; h_items (may be NULL) receives 8 * count
+ * int32 (the items, as in ws_work_offset) and must hold 8 * plan->work_capacity.
  */
 mla_status_t mla_debug_read_work_list(const mla_plan_t* plan, const void* d_workspace, int32_t* h_count,
                                       int32_t* h_items);

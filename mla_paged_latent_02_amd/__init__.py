@@ -282,14 +282,15 @@ def read_plan_arrays(plan: Plan, workspace):
 
 
 def read_work_list(plan: Plan, workspace):
-    """The planner's work list, [(sequence, chunk), ...] in dispatch order, copied synchronously."""
+    """The planner's work list in hand-out order, copied synchronously: one 8-tuple per item
+    (sequence, chunk, planned ctx, page-list start, n_b, first partial record, 0, 0)."""
     count = ctypes.c_int32(0)
-    items = (ctypes.c_int32 * (2 * max(1, plan.work_capacity)))()
+    items = (ctypes.c_int32 * (8 * max(1, plan.work_capacity)))()
     st = _lib.mla_debug_read_work_list(ctypes.byref(plan), _ptr(workspace), ctypes.cast(ctypes.byref(count), ctypes.c_void_p),
                                        ctypes.cast(items, ctypes.c_void_p))
     if st != MLA_OK:
         raise MlaError("mla_debug_read_work_list", st)
-    return [(items[2 * i], items[2 * i + 1]) for i in range(count.value)]
+    return [tuple(items[8 * i:8 * i + 8]) for i in range(count.value)]
 
 
 def plan_to_dict(plan: Plan) -> dict:

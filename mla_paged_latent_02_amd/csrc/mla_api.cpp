@@ -139,7 +139,8 @@ mla_status_t mla_debug_read_work_list(const mla_plan_t* plan, const void* d_work
   if (int64_t(words[1]) > plan->work_capacity) return MLA_ERR_BAD_PLAN;
   *h_count = int32_t(words[1]);
   if (h_items && words[1] > 0 &&
-      hipMemcpy(h_items, ws + plan->ws_work_offset, size_t(words[1]) * 8, hipMemcpyDeviceToHost) != hipSuccess)
+      hipMemcpy(h_items, ws + plan->ws_work_offset, size_t(words[1]) * mla::kItemWords * 4, hipMemcpyDeviceToHost) !=
+          hipSuccess)
     return MLA_ERR_HIP;
   return MLA_OK;
 }

@@ -13,6 +13,7 @@ constexpr int kBlockRows = 64;             // chunks are multiples of this many 
 constexpr int kMaxTileRows = 128;
 constexpr int kMaxSeqlenQo = MLA_MAX_SEQLEN_QO;
 constexpr int kNumXcd = 8;                 // the hardware deals consecutive workgroups to 8 XCDs in turn
+constexpr int kItemWords = 8;              // work item: b, chunk, ctx, page start, n_b, first record, 0, 0
 
 // Everything one decode launch needs, passed by value.
 struct DecodeArgs {
@@ -23,7 +24,7 @@ struct DecodeArgs {
   const int32_t* context_lens;  // [B]
   const int32_t* nchunks;       // [B] from the planner
   const int32_t* partbase;      // [B] from the planner
-  const int32_t* work;          // [capacity][2] (sequence, chunk) items from the planner
+  const int32_t* work;          // [capacity][8] work items from the planner
   uint32_t* status;             // [0] status bits, [1] item count, [2] task counter, [3] finished workgroups
   uint16_t* out;                // bf16 [B, S, H, 512]
   float* lse;                   // [B, S, H] or null

@@ -109,13 +109,16 @@ struct SeqWork {
   int32_t nfull;  // chunks of exactly chunk_len rows
   int32_t cat;    // -1: none; 0..15: length class of the partial last chunk; 16: invalid
   uint32_t bad;   // status bits
+  int32_t ctx, page_base;
 };
 
 __device__ __forceinline__ SeqWork seq_work(const PlanArgs& a, int b) {
-  SeqWork w{0, 0, -1, 0u};
+  SeqWork w{0, 0, -1, 0u, 0, 0};
   if (b >= a.batch) return w;
   const int32_t ctx = a.context_lens[b];
-  const int32_t pages = a.kv_indptr[b + 1] - a.kv_indptr[b];
+  w.ctx = ctx;
+  w.page_base = a.kv_indptr[b];
+  const int32_t pages = a.kv_indptr[b + 1] - w.page_base;
   if (ctx < a.seqlen_qo) w.bad |= MLA_DEV_CTX_TOO_SHORT;
   if (ctx > a.max_context_len) w.bad |= MLA_DEV_CTX_TOO_LONG;
   if (!w.bad && (int64_t)pages * a.page_size < (int64_t)ctx) w.bad |= MLA_DEV_TOO_FEW_PAGES;
@@ -131,8 +134,28 @@ __device__ __forceinline__ SeqWork seq_work(const PlanArgs& a, int b) {
   return w;
 }
 
+// Work item `pos` of the list: the chunk and, so that a decode task needs no
+// second round trip for them, its sequence's planned length, page-list start,
+// chunk count and first partial record.
+__device__ __forceinline__ void store_item(int32_t* work, int64_t pos, int32_t b, int32_t chunk, int32_t ctx,
+                                           int32_t page_base, int32_t n, int32_t part_base) {
+  u32x4_t lo, hi;
+  lo[0] = (uint32_t)b;
+  lo[1] = (uint32_t)chunk;
+  lo[2] = (uint32_t)ctx;
+  lo[3] = (uint32_t)page_base;
+  hi[0] = (uint32_t)n;
+  hi[1] = (uint32_t)part_base;
+  hi[2] = 0;
+  hi[3] = 0;
+  u32x4_t* dst = (u32x4_t*)(work + pos * kItemWords);
+  dst[0] = lo;
+  dst[1] = hi;
+}
+
 __global__ __launch_bounds__(256) void mla_plan_kernel(PlanArgs a) {
   __shared__ int32_t scan_pb[256], scan_full[256];
+  __shared__ int32_t t_ctx[256], t_pb[256], t_n[256], t_base[256];  // the tile's sequence fields
   __shared__ int32_t cat_wave[4][kCats];
   __shared__ int32_t cat_total[kCats], cat_base[kCats], cat_carry[kCats];
   __shared__ int32_t full_total;
@@ -192,6 +215,12 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(PlanArgs a) {
       scan_full[tid] += v1;
       __syncthreads();
     }
+    const int32_t my_base = carry_pb + scan_pb[tid] - contrib;
+    t_ctx[tid] = w.ctx;
+    t_pb[tid] = w.page_base;
+    t_n[tid] = w.n;
+    t_base[tid] = my_base;
+    __syncthreads();
     // the tile's full chunks, spread over all threads: item i of the tile is chunk
     // i - (first item of j) of the tile's sequence j, the first j whose inclusive count
     // exceeds i (a long sequence's chunks are not written by one thread alone)
@@ -203,19 +232,15 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(PlanArgs a) {
         if (scan_full[mid] > i) hi = mid; else lo = mid + 1;
       }
       const int32_t first = lo > 0 ? scan_full[lo - 1] : 0;
-      i32x2_t item;
-      item[0] = base + lo;
-      item[1] = i - first;
-      *(i32x2_t*)(a.work + 2 * (int64_t)(carry_full + i)) = item;
+      store_item(a.work, carry_full + i, base + lo, i - first, t_ctx[lo], t_pb[lo], t_n[lo], t_base[lo]);
     }
     if (b < a.batch) {
       a.nchunks[b] = w.n;
-      a.partbase[b] = carry_pb + scan_pb[tid] - contrib;
+      a.partbase[b] = my_base;
       if (w.cat >= 0) {
         int32_t pos = cat_base[w.cat] + cat_carry[w.cat] + rank;
         for (int v = 0; v < wave; ++v) pos += cat_wave[v][w.cat];
-        a.work[2 * pos] = b;
-        a.work[2 * pos + 1] = w.cat == kLengthClasses ? -1 : w.n - 1;
+        store_item(a.work, pos, b, w.cat == kLengthClasses ? -1 : w.n - 1, w.ctx, w.page_base, w.n, my_base);
       }
     }
     carry_pb += scan_pb[255];
@@ -645,6 +670,17 @@ struct DecodeCfg {
   static_assert(kTaskSlotBase % 16 == 0 && kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
+// A work item as the planner writes it: the chunk and its sequence's planned fields.
+struct TaskItem {
+  int32_t b, chunk, ctx, page_base, n_b, rec_base;
+};
+
+__device__ __forceinline__ TaskItem load_item(const DecodeArgs& a, int item) {
+  const int32_t* w = a.work + (int64_t)item * kItemWords;
+  TaskItem t{w[0], w[1], w[2], w[3], w[4], w[5]};
+  return t;
+}
+
 // The next untaken task of the list: a device-scope vector atomic on the task
 // counter (the planner starts it at W, the grid's first tasks being below W).
 __device__ __forceinline__ int take_task(const DecodeArgs& a) {
@@ -661,7 +697,7 @@ __device__ __forceinline__ int take_task(const DecodeArgs& a) {
 // fp8 MFMA as they are (one term, unit block scale; the per-tensor q scale is
 // folded into the softmax scale) and its rope dims are widened exactly to bf16.
 template <bool FP8, int HW, int KW, int NS, int WPE, int KD, int VD, int QC, bool QF8>
-__device__ __forceinline__ void decode_task(const DecodeArgs& a, LDS_PTR(uint8_t) lds, int b, int chunk, int grp,
+__device__ __forceinline__ void decode_task(const DecodeArgs& a, LDS_PTR(uint8_t) lds, const TaskItem& it, int grp,
                                             int& nxt) {
   static_assert(FP8 || !QF8, "an fp8 query needs an fp8 cache");
   using Cfg = DecodeCfg<FP8, HW, KW, NS>;
@@ -681,24 +717,18 @@ __device__ __forceinline__ void decode_task(const DecodeArgs& a, LDS_PTR(uint8_t
   const int i16 = lane & 15;  // MFMA column: head row within the wave's 16-row tile
   const int g4 = lane >> 4;   // MFMA k-group
 
-  // ---- work item (b, chunk), loaded by the caller. Every load before the first
-  // cache row is a cold round trip, so they go in three dependent batches: the
-  // item, then the sequence's fields, then its first page ids together with the
-  // query. The empty asm statements keep the compiler from spreading a batch
-  // over several waits.
+  // ---- work item, loaded by the caller with the sequence's planned fields, so
+  // that the loads before the first cache row are two batches of cold round
+  // trips: the item, then the first page ids together with the query (and the
+  // live context length, checked against the planned one).
+  const int b = it.b, chunk = it.chunk;
   if (chunk < 0) {  // invalid sequence: NaN rows
     if (wave == 0 && lane == 0) nxt = take_task(a);
     fill_invalid_rows(a, b, grp, wave, NW, lane);
     return;
   }
-  const int ctx = a.context_lens[b];
-  const int page_base = a.kv_indptr[b];
-  const int n_b = a.nchunks[b];
-  const int rec_base = a.partbase[b];
-  asm volatile("" ::"s"(ctx), "s"(page_base), "s"(n_b), "s"(rec_base));
-  // a context that grew past the planned chunk count would lose its last rows: flag the plan
-  if ((ctx + a.chunk_len - 1) / a.chunk_len != n_b && chunk == 0 && grp == 0 && wave == 0 && lane == 0)
-    atomicOr(a.status, MLA_DEV_STALE_PLAN);
+  const int ctx = it.ctx, page_base = it.page_base, n_b = it.n_b, rec_base = it.rec_base;
+  const int live_ctx = a.context_lens[b];
 
   const int c_start = chunk * a.chunk_len;
   const int c_end = min(c_start + a.chunk_len, ctx);
@@ -841,6 +871,9 @@ __device__ __forceinline__ void decode_task(const DecodeArgs& a, LDS_PTR(uint8_t
     v_base_hi = (uint32_t)(16 + 4 * g4 + k) * L::kMainStride + 8u * c;
   }
 
+  // the live context length came with the query: the plan holds for the lengths it was made with
+  asm volatile("" ::"s"(live_ctx));
+  if (live_ctx != ctx && chunk == 0 && grp == 0 && wave == 0 && lane == 0) atomicOr(a.status, MLA_DEV_STALE_PLAN);
   gather.start();
   const float sscale = a.score_scale_log2;
   // Wave priority: two waves share each SIMD, and while one runs its softmax
@@ -1101,10 +1134,9 @@ void mla_decode_kernel(DecodeArgs a) {
   // the item count with the first task's item, in one batch (the item index is clamped to
   // the list's capacity, so a workgroup past the list still reads in bounds)
   const int n_items = (int)a.status[1];
-  const int item0 = min(task / G, a.work_capacity - 1);
-  int b = a.work[2 * item0];
-  int chunk = a.work[2 * item0 + 1];
-  asm volatile("" ::"s"(n_items), "s"(b), "s"(chunk));
+  TaskItem cur = load_item(a, min(task / G, a.work_capacity - 1));
+  asm volatile("" ::"s"(n_items), "s"(cur.b), "s"(cur.chunk), "s"(cur.ctx), "s"(cur.page_base), "s"(cur.n_b),
+               "s"(cur.rec_base));
   const int n_tasks = n_items * G;
   for (int k = 0; task < n_tasks; ++k) {
     int nxt = 0;
@@ -1118,7 +1150,7 @@ void mla_decode_kernel(DecodeArgs a) {
     asm volatile("" : "+s"(ap));
     const int grp = task - (task / G) * G;
     LDS_PTR(int32_t) slot = (LDS_PTR(int32_t))(lds + Cfg::kTaskSlotBase) + (k & 1);
-    decode_task<FP8, HW, KW, NS, WPE, KD, VD, QC, QF8>(*(const DecodeArgs*)ap, lds, b, chunk, grp, nxt);
+    decode_task<FP8, HW, KW, NS, WPE, KD, VD, QC, QF8>(*(const DecodeArgs*)ap, lds, cur, grp, nxt);
     if (wave == 0 && lane == 0) {
       *slot = nxt;
       if (nxt == W + n_tasks - 1)  // the call's last value: every workgroup has taken its last
@@ -1129,10 +1161,9 @@ void mla_decode_kernel(DecodeArgs a) {
     __syncthreads();
     task = __builtin_amdgcn_readfirstlane(*slot);
     if (task < n_tasks) {
-      const int item = task / G;
-      b = a.work[2 * item];
-      chunk = a.work[2 * item + 1];
-      asm volatile("" ::"s"(b), "s"(chunk));
+      cur = load_item(a, task / G);
+      asm volatile("" ::"s"(cur.b), "s"(cur.chunk), "s"(cur.ctx), "s"(cur.page_base), "s"(cur.n_b),
+                   "s"(cur.rec_base));
     }
   }
 }
@@ -1310,11 +1341,25 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineArgs a) {
   const float total = total_lds;
   const float inv = total > 0.0f ? 1.0f / total : 0.0f;
   const int64_t orow = ((int64_t)b * a.seqlen_qo + s) * a.num_heads + head;
-  for (int cc = tid; cc < CB; cc += 256) {
+  if constexpr (CB < 256) {
+    // R consecutive threads per column, each summing every R-th stream, then
+    // shuffled together (a serial sum of all the streams per column would be
+    // kStreams dependent LDS round trips)
+    constexpr int R = 256 / CB;
+    const int cc = tid / R, part = tid % R;
     float v = 0.0f;
+#pragma unroll
+    for (int st = part; st < kStreams; st += R) v += w_lds[st] * acc_lds[st][cc];
+#pragma unroll
+    for (int off = R / 2; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    if (part == 0) a.out[orow * kLatentDim + colblk * CB + cc] = __builtin_bit_cast(uint16_t, (__bf16)(v * inv));
+  } else {
+    for (int cc = tid; cc < CB; cc += 256) {
+      float v = 0.0f;
 #pragma unroll 8
-    for (int st = 0; st < kStreams; ++st) v += w_lds[st] * acc_lds[st][cc];
-    a.out[orow * kLatentDim + colblk * CB + cc] = __builtin_bit_cast(uint16_t, (__bf16)(v * inv));
+      for (int st = 0; st < kStreams; ++st) v += w_lds[st] * acc_lds[st][cc];
+      a.out[orow * kLatentDim + colblk * CB + cc] = __builtin_bit_cast(uint16_t, (__bf16)(v * inv));
+    }
   }
 }
 

@@ -160,7 +160,7 @@ mla_status_t mla_decode_plan_host(const mla_decode_params_t* params, const mla_p
   plan.ws_part_lse_offset = off;
   off = align256(off + uint64_t(plan.partial_capacity_records) * uint64_t(rows) * 4);
   plan.ws_work_offset = off;
-  off = align256(off + uint64_t(plan.work_capacity) * 8);
+  off = align256(off + uint64_t(plan.work_capacity) * mla::kItemWords * 4);
   plan.ws_bytes = off;
   *out_plan = plan;
   return MLA_OK;

@@ -83,7 +83,9 @@ def check_plan_arrays(case, dec):
     items = oracle.work_list(ref, rn, case.context_lens)
     assert n == rn and base == rbase
     assert status == oracle.status_words(ref, rbits, len(items))
-    assert mla.read_work_list(dec.plan, dec.workspace) == items
+    # each item: the (sequence, chunk) of the list, then its sequence's planned fields
+    want = [(b, c, int(case.context_lens[b]), int(case.kv_indptr[b]), rn[b], rbase[b], 0, 0) for b, c in items]
+    assert mla.read_work_list(dec.plan, dec.workspace) == want
     return status[0]
 
 
@@ -233,23 +235,25 @@ def test_counters_are_reset_after_every_call():
 
 
 def test_stale_plan_is_flagged():
-    # planned for one set of lengths, decoded with one sequence grown past its planned chunk
-    # count (a decode step without re-planning): the status bit is set. A sequence that grows
-    # within its chunk count is decoded in full and raises nothing.
+    # planned for one set of lengths, decoded with one sequence a row longer (a decode step
+    # without re-planning): the status bit is set and the call computes with the planned
+    # lengths, bit for bit what it gave before; re-planned, the bit is clear again
     import mla_paged_latent_02_amd as mla
     case = make_case(batch=3, seqlen_qo=1, num_heads=16, ctx=[300, 128, 500], page_size=16, kv_dtype="bf16",
                      seed=85, pool_pages=64)
     dec, out, lse = run(case, options(force_chunk=128))
     assert check_plan_arrays(case, dec) == 0
     inp = dec.inputs
-    inp.context_lens[0] += 1  # 301 rows: still three chunks of 128
+    inp.context_lens[0] += 1  # 301 rows: its 19 pages of 16 hold them
+    dec.out.fill_(float("nan"))
+    out2, _ = dec()
+    torch.cuda.synchronize()
+    assert mla.read_plan_arrays(dec.plan, dec.workspace)[2][0] == mla.DEV_STALE_PLAN
+    assert np.array_equal(out2.float().cpu().numpy().view(np.uint32), out.view(np.uint32))
+    dec.plan = mla.decode_plan(inp.params, inp.context_lens, inp.kv_indptr, dec.workspace, options(force_chunk=128))
     dec()
     torch.cuda.synchronize()
     assert mla.read_plan_arrays(dec.plan, dec.workspace)[2][0] == 0
-    inp.context_lens[1] += 1  # 129 rows: two chunks, one planned
-    dec()
-    torch.cuda.synchronize()
-    assert mla.read_plan_arrays(dec.plan, dec.workspace)[2][0] == mla.DEV_STALE_PLAN
 
 
 def test_run_to_run_bitwise_determinism():
