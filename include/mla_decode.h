@@ -358,7 +358,9 @@ typedef struct {
  *   d_v_out bf16 [num_out_rows, H, 128]        d_status uint32 or NULL: MLA_KVB_* bits are OR-ed in
  * Output rows that belong to no sequence are left untouched. Every buffer is
  * contiguous, 16-byte aligned and owned by the caller. Host-detectable errors
- * return before any device work; B = 0 or max_context_len = 0 does nothing.
+ * return before any device work; B = 0 or max_context_len = 0 does nothing;
+ * MLA_ERR_UNSUPPORTED when B * ceil(max_context_len / 256) * H >= 2^31 (the
+ * programs of 256 cached rows and one head are counted in 32 bits).
  */
 mla_status_t mla_gather_kv_b_proj(const mla_kv_b_proj_params_t* params, const void* d_kv_cache,
                                   const int32_t* d_kv_indptr, const int32_t* d_kv_page_indices,

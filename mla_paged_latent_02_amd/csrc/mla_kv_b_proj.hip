@@ -1,26 +1,44 @@
 // Cached-prefix expansion of the paged latent cache into per-head K and V.
 //
 // "perf(mla): chunk the non-FP4 gather_kv_b_proj over KV" (description): the
-// whole cached context is expanded once per layer, one program per (batch,
-// head, KV chunk), a program past its sequence's last chunk exiting at once.
-// Here a program is one workgroup of 4 waves that computes, for 128 cached rows
-// of one sequence and one head h, the 256 projections W[h] . c (128 K-nope then
-// 128 V) on bf16 MFMA (16x16x32), and copies the 64 rope values beside K.
+// whole cached context is expanded once per layer as a set of (sequence, KV
+// chunk, head) programs, none working past its sequence's end. Here a program
+// is 256 cached rows of one sequence and one head h: the 256 projections W[h].c
+// (128 K-nope then 128 V) on bf16 MFMA (16x16x32), and the 64 rope values
+// copied beside K.
 //
-//   * The latent (512 wide) streams through LDS in 8 stages of 64 columns,
-//     together with the matching 256 x 64 slice of W[h]: global -> registers
-//     (the next stage is loaded while the current one is multiplied) ->
-//     LDS. An fp8 cache is widened to bf16 on the way (exactly: every e4m3fn
-//     value is a bf16 value); kv_scale multiplies the float32 result.
-//   * Wave w owns output rows 128 (w & 1) .. +127 of W[h] (so K or V) for the
-//     cached rows 64 (w >> 1) .. +63 of the chunk: 8 x 4 accumulator tiles,
-//     turned into whole output rows in LDS before they are stored.
-//   * Program ids are spread so that each XCD walks a contiguous run of them in
-//     (sequence, chunk, head) order: the heads of one chunk run back to back on
-//     one XCD and share its L2 copy of the latent rows.
+//   * Persistent: one workgroup of 8 waves per CU walks a static share of the
+//     programs (XCD-contiguous, so that the workgroups of one XCD run adjacent
+//     programs and share its L2 copy of W[h] and of the latent rows). Reading
+//     W[h] once per 256 rows halves the L2 traffic of 128-row programs; the 8
+//     waves hold a 256 x 256 output tile (wave w: W rows 128 (w & 1) .. +127 for
+//     cached rows 64 (w >> 1) .. +63).
+//   * Each cached row is walked in slabs of KC columns (64 for an fp8 cache, 32
+//     for bf16): 512 / KC stages multiply a slab of W[h] and of the chunk's 256
+//     latent rows (fp8 kept as bytes and widened exactly to bf16 at the operand
+//     read; kv_scale multiplies the float32 result), then 64 / KC stages carry
+//     only the rope slab, stored as it arrives. The slabs are copied by
+//     global_load_lds DMA into a ring of LDS stages (3 for fp8, 4 for bf16) that
+//     runs on across program boundaries, so the copy never drains between
+//     programs. The copy rate of a CU is set by the number of distinct cache
+//     lines it requests: a 64-column W slab reads whole 128-byte lines. Each
+//     wave issues its share of every stage's copies and waits for them with
+//     counts of its own; the workgroup barrier then publishes the stage. Each
+//     16-byte piece of a row sits XOR-swizzled by row, so the operand reads hit
+//     distinct banks.
+//   * Wave 0 also copies, ahead of time, each program's page-list window and
+//     the sequence bounds of the programs to come (64 at a time), finds the
+//     next valid program two programs ahead and works out its row slots, so no
+//     wave ever waits on a dependent load. Results are stored straight from
+//     registers, 8 consecutive output columns per lane.
+//   * Rows past a chunk are copied from a valid row and never stored; rows with
+//     no valid slot are zeroed in LDS after they land (such a row reads as
+//     zeros) and flag a status bit.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
+#include <mutex>
 
 #include "mla_internal.h"
 
@@ -35,21 +53,53 @@ typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2_t;
 
 #define KVB_LDS(T) __attribute__((address_space(3))) T*
 
-constexpr int kChunkRows = 128;                      // cached rows per program
+constexpr int kChunkRows = 256;                      // cached rows per program
 constexpr int kWRows = 256;                          // rows of W[h]: K nope, then V
 constexpr int kNope = 128, kVDim = 128, kRope = 64;  // K is 192 wide: nope then rope
-constexpr int kStageCols = 64;                       // latent columns per stage
-constexpr int kStages = kLatentDim / kStageCols;     // 8
-constexpr int kRowBytes = kStageCols * 2;            // bf16 bytes of one row in a stage
-constexpr int kWLdsBytes = kWRows * kRowBytes;       // 32 KB
-constexpr int kLatLdsBytes = kChunkRows * kRowBytes; // 16 KB
+constexpr int kWaves = 8;
 constexpr int kXcds = 8;
-// Epilogue: each wave turns its 128 x 64 tile into bf16 rows of 256 bytes in LDS
-// (one row per cached row, 16 bytes of padding against bank conflicts), then
-// stores them 16 bytes per lane, 16 lanes per output row.
-constexpr int kEpRowBytes = kNope * 2 + 16;
-constexpr int kEpWaveBytes = 64 * kEpRowBytes;
-constexpr int kLdsBytes = (kWLdsBytes + kLatLdsBytes) > 4 * kEpWaveBytes ? (kWLdsBytes + kLatLdsBytes) : 4 * kEpWaveBytes;
+constexpr int kWindow = 64;     // programs whose sequence bounds one copy fetches
+constexpr int kLatSlab = 64;    // bytes of a latent row per stage (64 fp8 or 32 bf16 columns)
+constexpr int kPageStages = 4;  // stages that carry a quarter each of the next program's page-list window
+
+template <bool FP8>
+struct KvbCfg {
+  static constexpr int kElem = FP8 ? 1 : 2;
+  static constexpr int kRowBytes = kRowDim * kElem;
+  static constexpr int KC = kLatSlab / kElem;                // columns per stage: 64 | 32
+  static constexpr int kMfmaStages = kLatentDim / KC;        // 8 | 16
+  static constexpr int kStages = kRowDim / KC;               // 9 | 18: the rope is the last 64 / KC
+  static constexpr int kKSteps = KC / 32;                    // MFMA k-steps per stage: 2 | 1
+  static constexpr int kWRowBytes = KC * 2;                  // bytes of a W row per stage: 128 | 64
+  static constexpr int kWSlabBytes = kWRows * kWRowBytes;    // 32 KB | 16 KB
+  static constexpr int kWRowsPerInst = 1024 / kWRowBytes;    // 8 | 16
+  static constexpr int kWInsts = kWSlabBytes / 1024;         // 32 | 16
+  static constexpr int kWPerWave = kWInsts / kWaves;         // 4 | 2
+  static constexpr int kLatInsts = kChunkRows * kLatSlab / 1024;  // 16: row 16 j + lane / 4
+  static constexpr int kLatPerWave = kLatInsts / kWaves;          // 2
+  static constexpr int kRing = FP8 ? 3 : 4;
+  static constexpr int kStageBytes = kWSlabBytes + kChunkRows * kLatSlab;
+  static constexpr int kPageOff = kRing * kStageBytes;           // one program's page-list window
+  static constexpr int kSlotOff = kPageOff + kChunkRows * 4;     // two programs' row slots
+  static constexpr int kWinOff = kSlotOff + 2 * kChunkRows * 4;  // two windows of sequence bounds
+  static constexpr int kProgOff = kWinOff + 2 * 4 * kWindow * 4;  // four program records of 8 words
+  static constexpr int kLdsBytes = kProgOff + 4 * 32;
+  // copies a wave issues with stage s of a program: its share of the W slab (MFMA stages), of the
+  // latent slab and, for wave 0 (cls 0) on the first stages, a quarter of the next program's
+  // page-list window
+  static constexpr int wave_insts(int cls, int s) {
+    return (s < kMfmaStages ? kWPerWave : 0) + kLatPerWave + (s < kPageStages && cls == 0 ? 1 : 0);
+  }
+  // a wave's copies issued after its stage-s copies while stage s is waited for
+  static constexpr int wait_after(int cls, int s) {
+    int n = 0;
+    for (int u = 1; u <= kRing - 2; ++u) n += wave_insts(cls, (s + u) % kStages);
+    return n;
+  }
+  static_assert(kWInsts % kWaves == 0 && kLatInsts % kWaves == 0, "copy shares");
+  static_assert(kStages > kPageStages + kRing, "page-list window and slots are ready in time");
+  static_assert(kLdsBytes <= 160 * 1024, "LDS");
+};
 
 struct KvbArgs {
   const uint8_t* cache;
@@ -62,15 +112,71 @@ struct KvbArgs {
   uint32_t* status;
   int64_t num_slots;
   int64_t num_out_rows;
-  int64_t programs;   // batch * chunks * heads
-  int32_t num_heads, page_size, chunks, max_ctx;
+  int32_t programs;  // batch * chunks * heads (< 2^31)
+  int32_t num_heads, page_size, chunks, max_ctx, head_block;
+  uint32_t page_magic;  // floor((2^32 - 1) / page_size): n / page_size = umulhi(n, magic), then one correction
   float kv_scale;
 };
 
-// Byte offset of 16-byte chunk c (0..7) of LDS row r. The XOR keeps 8 and 16
-// consecutive rows read at one chunk on distinct 16-byte bank groups.
-__device__ __forceinline__ uint32_t swz(int r, int c) {
-  return (uint32_t)(r * kRowBytes + ((c ^ ((r & 7) ^ ((r >> 3) & 1))) << 4));
+// n / page_size for 0 <= n < 2^31
+__device__ __forceinline__ int kvb_page_div(int n, const KvbArgs& a) {
+  uint32_t q = __umulhi((uint32_t)n, a.page_magic);
+  if ((q + 1) * (uint32_t)a.page_size <= (uint32_t)n) ++q;
+  return (int)q;
+}
+
+// A program as the workgroup's waves see it (8 words in LDS); bad: some row has no valid slot.
+struct KvbProg {
+  int32_t valid, h, orow, nrows, r0, pg_first, pg_end, bad;
+};
+
+// 16-byte piece swizzles (physical piece = logical piece ^ swizzle(row)). W rows are read 16
+// at a time in the order that puts 8 consecutive output columns in one lane (rows 0-3, 8-11,
+// 16-19, 24-27 of a 32-row block): with 128-byte rows the rows of one parity need distinct
+// swizzles, with 64-byte rows distinct (row & 3, swizzle) pairs. Latent rows (64 bytes) are
+// read 16 consecutive at a time: distinct (row & 3, swizzle) pairs.
+template <bool FP8>
+__device__ __forceinline__ int sw_w(int r) {
+  if constexpr (FP8) return ((r >> 1) & 1) | ((r >> 2) & 6);
+  else return (r >> 3) & 3;
+}
+__device__ __forceinline__ int sw_lat(int r) { return (r >> 2) & 3; }
+
+// Copies from global memory straight into LDS (M0 = the wave's LDS base, the same in every
+// lane): 16 bytes per lane at lds_addr + 16 * lane from a 64-bit address, or from a scalar
+// base plus a 32-bit lane offset; 4 bytes per lane at lds_addr + 4 * lane. Inline asm, so
+// that the compiler does not guard LDS reads with waits of its own: each wave waits for its
+// copies with explicit counts before the barrier that publishes a stage.
+__device__ __forceinline__ void kvb_dma16(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
+__device__ __forceinline__ void kvb_dma16s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
+__device__ __forceinline__ void kvb_dma4(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
+
+// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void kvb_wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// wait for a wave's stage-s copies: wait_after(CLS, s) younger copies may still be in flight
+template <typename C, int CLS, int S = 0>
+__device__ __forceinline__ void kvb_wait_stage(int s) {
+  if constexpr (S < C::kStages) {
+    if (s == S) kvb_wait_vmcnt<C::wait_after(CLS, S)>();
+    else kvb_wait_stage<C, CLS, S + 1>(s);
+  }
 }
 
 template <bool HI>
@@ -86,95 +192,291 @@ __device__ __forceinline__ unsigned pack2(float a, float b) {
   return __builtin_bit_cast(unsigned, r);
 }
 
-template <bool FP8>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_kv_b_proj_kernel(KvbArgs a) {
-  // program id -> (sequence, chunk, head), XCD-contiguous
-  const int64_t per_xcd = (int64_t)gridDim.x / kXcds;
-  const int64_t pid = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  if (pid >= a.programs) return;
-  const int h = (int)(pid % a.num_heads);
-  const int64_t bc = pid / a.num_heads;
-  const int chunk = (int)(bc % a.chunks);
-  const int b = (int)(bc / a.chunks);
-  const int row0 = a.cu_ctx[b];
-  const int ctx = a.cu_ctx[b + 1] - row0;
-  const int r0 = chunk * kChunkRows;
-  if (row0 < 0 || ctx < 0 || (int64_t)row0 + ctx > a.num_out_rows) {  // rows outside the outputs: none written
-    if (chunk == 0 && h == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, MLA_KVB_ROWS_OUT_OF_RANGE);
-    return;
-  }
-  if (chunk == 0 && h == 0 && threadIdx.x == 0 && ctx > a.max_ctx && a.status)
-    atomicOr(a.status, MLA_KVB_CTX_TOO_LONG);  // rows past max_context_len are not written
-  const int lim = min(ctx, a.max_ctx);         // rows of this sequence that are expanded
-  if (r0 >= lim) return;                       // past this sequence's last chunk
-  const int nrows = min(kChunkRows, lim - r0);
+// program id -> (sequence, chunk, head): heads in blocks of head_block, then sequences, then
+// chunks, then the heads of the block, so that one XCD's adjacent programs share W[h] and the
+// latent rows of a chunk
+__device__ __forceinline__ void kvb_decode(const KvbArgs& a, int p, int& b, int& chunk, int& h) {
+  const int hb = a.head_block;
+  const int per_blk = a.programs / a.num_heads * hb;
+  const int blk = p / per_blk;
+  const int rem = p - blk * per_blk;
+  const int bc = rem / hb;
+  h = blk * hb + (rem - bc * hb);
+  b = bc / a.chunks;
+  chunk = bc - b * a.chunks;
+}
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
-  KVB_LDS(uint8_t) w_lds = (KVB_LDS(uint8_t))lds;
-  KVB_LDS(uint8_t) l_lds = w_lds + kWLdsBytes;
+template <bool FP8>
+__global__ __launch_bounds__(512) void mla_kv_b_proj_kernel(KvbArgs a) {
+  using C = KvbCfg<FP8>;
+  constexpr int S = C::kStages;
+  // The arguments are read from the kernarg segment where they are used, through a pointer
+  // the compiler cannot see through: hoisted to the top they would stay live in scalar
+  // registers around the whole loop and push the loop's registers into scratch.
+  typedef const __attribute__((address_space(4))) KvbArgs* KargPtr;
+  auto args = [&]() -> const KvbArgs& {
+    KargPtr ap = (KargPtr)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(ap));
+    return *(const KvbArgs*)ap;
+  };
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLdsBytes];
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+  KVB_LDS(uint8_t) L = (KVB_LDS(uint8_t))lds;
+  KVB_LDS(int32_t) prog_ring = (KVB_LDS(int32_t))(L + C::kProgOff);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
   const int nh = wave & 1, th = wave >> 1;
 
-  // the cached rows this thread stages: fp8 rows (tid >> 2) + 64 i, bf16 rows (tid >> 3) + 32 i
-  constexpr int kMyRows = FP8 ? 2 : 4;
-  constexpr int kRowStep = FP8 ? 64 : 32;
-  const int my_row0 = FP8 ? (tid >> 2) : (tid >> 3);
-  const int my_c = FP8 ? (tid & 3) : (tid & 7);  // 16-byte piece of the row's stage slice
-  constexpr int kElem = FP8 ? 1 : 2;
-  const uint8_t* src[kMyRows];
-  uint32_t bad = 0;
-  const int pg_first = max(a.kv_indptr[b], 0), pg_end = a.kv_indptr[b + 1];
-#pragma unroll
-  for (int i = 0; i < kMyRows; ++i) {
-    const int r = r0 + my_row0 + kRowStep * i;
-    src[i] = nullptr;
-    if (r < lim) {
-      const int q = r / a.page_size;
-      if (pg_first + q >= pg_end) {
-        bad |= MLA_KVB_TOO_FEW_PAGES;
-      } else {
-        const int64_t slot = (int64_t)a.kv_page_indices[pg_first + q] * a.page_size + (r - q * a.page_size);
-        if (slot < 0 || slot >= a.num_slots) bad |= MLA_KVB_SLOT_OUT_OF_RANGE;
-        else src[i] = a.cache + slot * (kRowDim * kElem) + my_c * 16;
+  // this workgroup's programs: candidates m = 0 .. count - 1 are programs first + m * step
+  // (XCD-contiguous ranges: the workgroups of one XCD take adjacent programs)
+  auto cand_first = [&]() -> int {
+    const int range = (args().programs + kXcds - 1) / kXcds;
+    return (int)(blockIdx.x % kXcds) * range + (int)(blockIdx.x / kXcds);
+  };
+  const int step = gridDim.x / kXcds;
+  int count;
+  {
+    const int range = (a.programs + kXcds - 1) / kXcds;
+    const int xcd = blockIdx.x % kXcds;
+    const int first = xcd * range + (int)(blockIdx.x / kXcds);
+    const int end = min(a.programs, (xcd + 1) * range);
+    count = first < end ? (end - first + step - 1) / step : 0;
+  }
+
+  // ---------------------------------------------------------------- wave 0's bookkeeping
+  // Program records are found two programs ahead from windows of 64 candidates' sequence
+  // bounds that wave 0 copies into LDS; the page-list window of a program is copied with the
+  // first four stages of the program before it, and its row slots are worked out at that
+  // program's stage 4.
+  uint32_t bits = 0;  // status bits found by this lane (wave 0)
+  int cand = 0;       // next candidate to examine
+  int win_issued = -1, win_ready = -1;
+
+  auto issue_window = [&](int w) {  // sequence bounds of candidates 64 w .. 64 w + 63
+    const KvbArgs& A = args();
+    const int m = w * kWindow + lane;
+    const int32_t* s0 = A.cu_ctx;
+    const int32_t* s1 = A.cu_ctx;
+    const int32_t* s2 = A.cu_ctx;
+    const int32_t* s3 = A.cu_ctx;
+    if (m < count) {
+      int b, chunk, h;
+      kvb_decode(A, cand_first() + m * step, b, chunk, h);
+      s0 = A.cu_ctx + b;
+      s1 = A.cu_ctx + b + 1;
+      s2 = A.kv_indptr + b;
+      s3 = A.kv_indptr + b + 1;
+    }
+    const uint32_t dst = lds_base + C::kWinOff + (uint32_t)(w & 1) * (4 * kWindow * 4);
+    kvb_dma4(s0, dst);
+    kvb_dma4(s1, dst + 256);
+    kvb_dma4(s2, dst + 512);
+    kvb_dma4(s3, dst + 768);
+  };
+  // the next valid program from candidate `cand` on (all lanes take the same path)
+  auto find_next = [&]() -> KvbProg {
+    KvbProg r = {};
+    while (cand < count) {
+      const KvbArgs& A = args();
+      const int w = cand / kWindow;
+      if (w + 1 > win_issued && (w + 1) * kWindow < count) {
+        issue_window(w + 1);
+        win_issued = w + 1;
       }
+      if (w > win_ready) {  // its copy may be in flight: wait for everything
+        kvb_wait_vmcnt<0>();
+        win_ready = win_issued;
+      }
+      KVB_LDS(int32_t) wb = (KVB_LDS(int32_t))(L + C::kWinOff + (w & 1) * (4 * kWindow * 4));
+      const int e = cand % kWindow;
+      const int32_t row0 = wb[e], row1 = wb[kWindow + e], pg0 = wb[2 * kWindow + e], pg1 = wb[3 * kWindow + e];
+      int b, chunk, h;
+      kvb_decode(A, cand_first() + cand * step, b, chunk, h);
+      ++cand;
+      const int ctx = row1 - row0;
+      if (row0 < 0 || ctx < 0 || (int64_t)row0 + ctx > A.num_out_rows) {  // rows outside the outputs
+        if (chunk == 0 && h == 0) bits |= MLA_KVB_ROWS_OUT_OF_RANGE;
+        continue;
+      }
+      if (chunk == 0 && h == 0 && ctx > A.max_ctx) bits |= MLA_KVB_CTX_TOO_LONG;  // rows past it not written
+      const int lim = min(ctx, A.max_ctx);
+      const int r0 = chunk * kChunkRows;
+      if (r0 >= lim) continue;  // past this sequence's last chunk
+      r = KvbProg{1, h, row0 + r0, min(kChunkRows, lim - r0), r0, max(pg0, 0), pg1, 0};
+      break;
+    }
+    return r;
+  };
+  auto publish = [&](const KvbProg& q, int slot) {  // program record -> LDS ring entry
+    if (lane == 0) {
+      KVB_LDS(int32_t) r = prog_ring + slot * 8;
+      r[0] = q.valid;
+      r[1] = q.h;
+      r[2] = q.orow;
+      r[3] = q.nrows;
+      r[4] = q.r0;
+      r[5] = q.pg_first;
+      r[6] = q.pg_end;
+      r[7] = q.bad;
+    }
+  };
+  auto ring_get = [&](int slot) -> KvbProg {  // a program record, as scalars
+    KVB_LDS(int32_t) r = prog_ring + slot * 8;
+    return KvbProg{__builtin_amdgcn_readfirstlane(r[0]), __builtin_amdgcn_readfirstlane(r[1]),
+                   __builtin_amdgcn_readfirstlane(r[2]), __builtin_amdgcn_readfirstlane(r[3]),
+                   __builtin_amdgcn_readfirstlane(r[4]), __builtin_amdgcn_readfirstlane(r[5]),
+                   __builtin_amdgcn_readfirstlane(r[6]), __builtin_amdgcn_readfirstlane(r[7])};
+  };
+  // page-list window copy j (ids 64 j .. 64 j + 63) of program q
+  auto issue_pages = [&](const KvbProg& q, int j) {
+    const KvbArgs& A = args();
+    const int32_t* src = A.cu_ctx;  // a harmless valid word when the id is not needed
+    if (q.valid) {
+      const int64_t gi = (int64_t)q.pg_first + kvb_page_div(q.r0, A) + j * 64 + lane;
+      if (gi < q.pg_end) src = A.kv_page_indices + gi;
+    }
+    kvb_dma4(src, lds_base + C::kPageOff + (uint32_t)j * 256);
+  };
+  // row slots of program q (ring entry `slot`) from its page-list window, 4 rows per lane of
+  // wave 0; records in the entry whether any row has no valid slot
+  auto make_slots = [&](int slot, int parity) {
+    const KvbProg q = ring_get(slot);
+    KVB_LDS(int32_t) pt = (KVB_LDS(int32_t))(L + C::kPageOff);
+    KVB_LDS(int32_t) st = (KVB_LDS(int32_t))(L + C::kSlotOff) + parity * kChunkRows;
+    const KvbArgs& A = args();
+    const int P = A.page_size;
+    const int npages = q.pg_end - q.pg_first;
+    const int page0 = kvb_page_div(q.r0, A);
+    bool any = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = lane + 64 * i;
+      const int ra = q.r0 + min(r, q.nrows - 1);
+      const int page = kvb_page_div(ra, A);
+      int32_t sl = -1;
+      if (page < npages) {
+        const int64_t v = (int64_t)pt[page - page0] * P + (ra - page * P);
+        if (v >= 0 && v < A.num_slots) sl = (int32_t)v;
+        else if (r < q.nrows) bits |= MLA_KVB_SLOT_OUT_OF_RANGE;
+      } else if (r < q.nrows) {
+        bits |= MLA_KVB_TOO_FEW_PAGES;
+      }
+      any |= sl < 0;
+      st[r] = sl;
+    }
+    const bool bad = __builtin_amdgcn_ballot_w64(any) != 0;  // over all 64 lanes, before the lane-0 store
+    if (lane == 0) prog_ring[slot * 8 + 7] = bad;
+  };
+
+  // ---------------------------------------------------------------- every wave's copies
+  // W copy j: row kWRowsPerInst j + lane / (64 / kWRowsPerInst), place lane % (64 / kWRowsPerInst),
+  // holding logical piece place ^ sw_w(row); this wave's are j = kWPerWave wave + i. Latent copy
+  // j: row 16 j + lane / 4, place lane % 4 holding logical piece place ^ sw_lat(row) (the same
+  // for every j: sw_lat(16 j + lane / 4) = (lane >> 4) & 3); this wave's are j = 2 wave, 2 wave + 1.
+  constexpr int kWLanesPerRow = 64 / C::kWRowsPerInst;  // 8 | 4
+  uint32_t w_off[C::kWPerWave];
+#pragma unroll
+  for (int i = 0; i < C::kWPerWave; ++i) {
+    const int j = C::kWPerWave * wave + i;
+    const int row = C::kWRowsPerInst * j + lane / kWLanesPerRow;
+    const int place = lane % kWLanesPerRow;
+    w_off[i] = (uint32_t)(row * (kLatentDim * 2) + ((place ^ sw_w<FP8>(row)) << 4));
+  }
+  const int lat_logical = (lane & 3) ^ ((lane >> 4) & 3);
+
+  // This wave's copies of stage s of program k (record in ring entry k & 3, slots in table
+  // k & 1) and, for wave 0 on the first stages, a quarter of program k + 1's page-list window:
+  // copy i < kWPerWave is a W piece (MFMA stages only), then kLatPerWave latent pieces, then the
+  // page-list piece. A stage's copies are issued one at a time between its MFMAs.
+  constexpr int kCopies = C::kWPerWave + C::kLatPerWave + 1;
+  struct Group {
+    bool on;                 // the stage exists
+    int s, k;
+    const uint8_t* wsrc;     // W slab base (scalar)
+    uint32_t stage;          // LDS stage base
+    const uint8_t* lat[C::kLatPerWave];
+  };
+  auto plan_group = [&](int k, int s, bool on) -> Group {
+    Group gr;
+    gr.on = on;
+    gr.s = s;
+    gr.k = k;
+    const KvbArgs& A = args();
+    gr.stage = lds_base + (uint32_t)(((k * S + s) % C::kRing) * C::kStageBytes);
+    const int32_t qh = __builtin_amdgcn_readfirstlane(prog_ring[(k & 3) * 8 + 1]);
+    gr.wsrc = (const uint8_t*)(A.w + (int64_t)qh * kWRows * kLatentDim) + s * C::kWRowBytes;
+    KVB_LDS(int32_t) st = (KVB_LDS(int32_t))(L + C::kSlotOff) + (k & 1) * kChunkRows;
+#pragma unroll
+    for (int i = 0; i < C::kLatPerWave; ++i) {
+      const int j = C::kLatPerWave * wave + i;
+      const int32_t sl = max(st[16 * j + (lane >> 2)], 0);
+      gr.lat[i] = A.cache + (int64_t)sl * C::kRowBytes + s * kLatSlab + lat_logical * 16;
+    }
+    return gr;
+  };
+  auto fire = [&](const Group& gr, int i) {
+    if (!gr.on) return;
+    if (i < C::kWPerWave) {
+      if (gr.s < C::kMfmaStages) kvb_dma16s(gr.wsrc, w_off[i], gr.stage + (uint32_t)(C::kWPerWave * wave + i) * 1024);
+    } else if (i < C::kWPerWave + C::kLatPerWave) {
+      const int j = C::kLatPerWave * wave + (i - C::kWPerWave);
+      kvb_dma16(gr.lat[i - C::kWPerWave], gr.stage + (uint32_t)(C::kWSlabBytes + j * 1024));
+    } else if (gr.s < kPageStages && wave == 0) {
+      issue_pages(ring_get((gr.k + 1) & 3), gr.s);
+    }
+  };
+  auto issue_group = [&](int k, int s) {
+    const Group gr = plan_group(k, s, true);
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) fire(gr, i);
+  };
+  // after this wave's stage-s copies of program k have landed: zero the latent pieces of rows
+  // with no valid slot
+  auto zero_bad = [&](int k, int s) {
+    KVB_LDS(int32_t) st = (KVB_LDS(int32_t))(L + C::kSlotOff) + (k & 1) * kChunkRows;
+    KVB_LDS(uint8_t) lat = L + ((k * S + s) % C::kRing) * C::kStageBytes + C::kWSlabBytes;
+#pragma unroll
+    for (int i = 0; i < C::kLatPerWave; ++i) {
+      const int j = C::kLatPerWave * wave + i;
+      if (st[16 * j + (lane >> 2)] < 0) *(KVB_LDS(u32x4_t))(lat + j * 1024 + lane * 16) = u32x4_t{0, 0, 0, 0};
+    }
+  };
+  auto wait_stage = [&](int s, bool full) {  // full: the younger stages were all issued
+    if (!full) kvb_wait_vmcnt<0>();
+    else if (wave == 0) kvb_wait_stage<C, 0>(s);
+    else kvb_wait_stage<C, 1>(s);
+  };
+
+  // ---------------------------------------------------------------- prologue
+  if (wave == 0) {
+    if (count > 0) {
+      issue_window(0);
+      win_issued = 0;
+      kvb_wait_vmcnt<0>();
+      win_ready = 0;
+    }
+    const KvbProg p0 = find_next();
+    const KvbProg p1 = p0.valid ? find_next() : KvbProg{};
+    publish(p0, 0);
+    publish(p1, 1);
+    publish(KvbProg{}, 2);
+    if (p0.valid) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) issue_pages(p0, j);
+      kvb_wait_vmcnt<0>();
+      win_ready = win_issued;
+      make_slots(0, 0);
     }
   }
-  if (bad && a.status) atomicOr(a.status, bad);
-
-  // W[h] slice this thread stages: rows (tid >> 3) + 32 i, 16-byte piece tid & 7
-  const uint16_t* wsrc = a.w + ((int64_t)h * kWRows + (tid >> 3)) * kLatentDim + (tid & 7) * 8;
-
-  u32x4_t wreg[8];
-  u32x4_t lreg[kMyRows];
-  auto load_stage = [&](int s) {
+  __syncthreads();
+  KvbProg cur = ring_get(0);  // the program being computed
+  if (cur.valid) {
+    // stages 0 .. kRing - 2 of program 0 (the first ones carry program 1's page-list window)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) wreg[i] = *(const u32x4_t*)(wsrc + (int64_t)i * 32 * kLatentDim + s * kStageCols);
-#pragma unroll
-    for (int i = 0; i < kMyRows; ++i)
-      lreg[i] = src[i] ? *(const u32x4_t*)(src[i] + s * kStageCols * kElem) : u32x4_t{0, 0, 0, 0};
-  };
-  auto store_stage = [&]() {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *(KVB_LDS(u32x4_t))(w_lds + swz((tid >> 3) + 32 * i, tid & 7)) = wreg[i];
-#pragma unroll
-    for (int i = 0; i < kMyRows; ++i) {
-      const int r = my_row0 + kRowStep * i;
-      if constexpr (FP8) {  // 16 fp8 -> two 16-byte bf16 pieces 2c, 2c+1
-        const u32x4_t v = lreg[i];
-        const u32x4_t lo = {fp8x2_bf16x2<false>(v[0]), fp8x2_bf16x2<true>(v[0]), fp8x2_bf16x2<false>(v[1]),
-                            fp8x2_bf16x2<true>(v[1])};
-        const u32x4_t hi = {fp8x2_bf16x2<false>(v[2]), fp8x2_bf16x2<true>(v[2]), fp8x2_bf16x2<false>(v[3]),
-                            fp8x2_bf16x2<true>(v[3])};
-        *(KVB_LDS(u32x4_t))(l_lds + swz(r, 2 * my_c)) = lo;
-        *(KVB_LDS(u32x4_t))(l_lds + swz(r, 2 * my_c + 1)) = hi;
-      } else {
-        *(KVB_LDS(u32x4_t))(l_lds + swz(r, my_c)) = lreg[i];
-      }
-    }
-  };
+    for (int s = 0; s < C::kRing - 1; ++s) issue_group(0, s);
+  }
 
   f32x4_t acc[8][4];
 #pragma unroll
@@ -182,82 +484,155 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) acc[nb][tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  load_stage(0);
-  for (int s = 0; s < kStages; ++s) {
-    __syncthreads();  // every wave is done reading the previous stage
-    store_stage();
+  int k = 0;
+  bool next_valid = false;
+  // entering stage s of program k: this wave's stage-s copies have landed once its younger
+  // copies are all that may be in flight; the barrier publishes the stage to every wave (and
+  // every wave is then done with stage s - 1, whose slot the copies issued here refill)
+  auto stage_begin = [&](int s) -> Group {
+    wait_stage(s, s + C::kRing - 2 < S || next_valid);
+    if (cur.bad) zero_bad(k, s);
     __syncthreads();
-    if (s + 1 < kStages) load_stage(s + 1);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int c = 4 * ks + g;  // this lane's 8 columns of the 32-column MFMA slab
-      bf16x8_t bt[4];
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-        bt[tb] = *(KVB_LDS(bf16x8_t))(l_lds + swz(th * 64 + tb * 16 + l16, c));
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const bf16x8_t at = *(KVB_LDS(bf16x8_t))(w_lds + swz(nh * 128 + nb * 16 + l16, c));
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) acc[nb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(at, bt[tb], acc[nb][tb], 0, 0, 0);
-      }
+    if (wave == 0 && s == kPageStages) {
+      // program k + 1's page-list window landed with the first stages: its row slots
+      if (next_valid) make_slots((k + 1) & 3, (k + 1) & 1);
     }
-  }
-
-  // acc[nb][tb][i]: W row nh*128 + nb*16 + 4g + i, cached row th*64 + tb*16 + l16
-  const int H = a.num_heads;
-  __syncthreads();  // every wave is done with the last stage: LDS becomes the epilogue buffer
-  KVB_LDS(uint8_t) ep = (KVB_LDS(uint8_t))lds + wave * kEpWaveBytes;
-#pragma unroll
-  for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const f32x4_t v = acc[nb][tb];
-      *(KVB_LDS(u32x2_t))(ep + (tb * 16 + l16) * kEpRowBytes + (nb * 16 + 4 * g) * 2) =
-          u32x2_t{pack2(v[0] * a.kv_scale, v[1] * a.kv_scale), pack2(v[2] * a.kv_scale, v[3] * a.kv_scale)};
+    if (wave == 0 && s == kPageStages + 1) {
+      // program k + 2 (its page-list window rides on program k + 1's first stages)
+      publish(next_valid ? find_next() : KvbProg{}, (k + 2) & 3);
     }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // this wave's copies of stage t (this program's or the next one's)
+    const int t = s + C::kRing - 1;
+    return t < S ? plan_group(k, t, true) : plan_group(k + 1, t - S, next_valid);
+  };
+  while (cur.valid) {
+    // whether a program follows (its record was written two programs ago)
+    next_valid = __builtin_amdgcn_readfirstlane(prog_ring[((k + 1) & 3) * 8]) != 0;
+    for (int s = 0; s < C::kMfmaStages; ++s) {
+      const Group gr = stage_begin(s);
+      // the stage's MFMAs: W rows nh*128 + perm(nb, l16), chunk rows th*64 + tb*16 + l16,
+      // k piece 4 ks + g of the stage's columns
+      KVB_LDS(uint8_t) ws = L + ((k * S + s) % C::kRing) * C::kStageBytes;
+      KVB_LDS(uint8_t) ls = ws + C::kWSlabBytes;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int tr = i * 4 + (lane >> 4), piece = lane & 15;  // wave-local row, 16-byte piece of its 256 bytes
-    const int t = th * 64 + tr;
-    if (t >= nrows) continue;
-    const u32x4_t o = *(KVB_LDS(u32x4_t))(ep + tr * kEpRowBytes + piece * 16);
-    const int64_t orow = (int64_t)row0 + r0 + t;
-    uint16_t* dst = nh == 0 ? a.k_out + (orow * H + h) * (kNope + kRope) : a.v_out + (orow * H + h) * kVDim;
-    *(u32x4_t*)(dst + piece * 8) = o;
-  }
-
-  // rope part of K: 128 rows x 8 pieces of 8 values, 4 per thread
+      for (int ks = 0; ks < C::kKSteps; ++ks) {
+        bf16x8_t bt[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int id = tid + 256 * i;
-    const int t = id >> 3, piece = id & 7;
-    if (t >= nrows) continue;
-    const int r = r0 + t;
-    const int q = r / a.page_size;
-    const int64_t slot = pg_first + q < pg_end
-                             ? (int64_t)a.kv_page_indices[pg_first + q] * a.page_size + (r - q * a.page_size)
-                             : -1;  // no page: the row reads as zeros, like its K-nope and V
-    u32x4_t o = {0, 0, 0, 0};
-    if (slot >= 0 && slot < a.num_slots) {
-      const uint8_t* p = a.cache + slot * (kRowDim * kElem) + (kLatentDim + piece * 8) * kElem;
-      if constexpr (FP8) {
-        const u32x2_t raw = *(const u32x2_t*)p;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const unsigned lo = fp8x2_bf16x2<false>(raw[j]), hi = fp8x2_bf16x2<true>(raw[j]);
-          o[2 * j] = pack2(__uint_as_float(lo << 16) * a.kv_scale, __uint_as_float(lo & 0xffff0000u) * a.kv_scale);
-          o[2 * j + 1] = pack2(__uint_as_float(hi << 16) * a.kv_scale, __uint_as_float(hi & 0xffff0000u) * a.kv_scale);
+        for (int tb = 0; tb < 4; ++tb) {
+          const int row = th * 64 + tb * 16 + l16;
+          if constexpr (FP8) {
+            const u32x2_t raw = *(KVB_LDS(u32x2_t))(ls + row * kLatSlab + (((2 * ks + (g >> 1)) ^ sw_lat(row)) << 4) +
+                                                     ((g & 1) << 3));
+            const u32x4_t v = {fp8x2_bf16x2<false>(raw[0]), fp8x2_bf16x2<true>(raw[0]), fp8x2_bf16x2<false>(raw[1]),
+                               fp8x2_bf16x2<true>(raw[1])};
+            bt[tb] = __builtin_bit_cast(bf16x8_t, v);
+          } else {
+            bt[tb] = *(KVB_LDS(bf16x8_t))(ls + row * kLatSlab + ((g ^ sw_lat(row)) << 4));
+          }
         }
-      } else {
-        o = *(const u32x4_t*)p;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          // tile nb's row m holds W row 32 (nb / 2) + 8 (m / 4) + 4 (nb % 2) + m % 4, so that a
+          // lane's results of tiles 2i and 2i + 1 are 8 consecutive output columns
+          const int wrow = nh * 128 + (nb >> 1) * 32 + ((l16 >> 2) << 3) + ((nb & 1) << 2) + (l16 & 3);
+          const bf16x8_t at =
+              *(KVB_LDS(bf16x8_t))(ws + wrow * C::kWRowBytes + (((4 * ks + g) ^ sw_w<FP8>(wrow)) << 4));
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb)
+            acc[nb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(at, bt[tb], acc[nb][tb], 0, 0, 0);
+          // the stage's copies, one after every other tile row of MFMAs
+          const int slot_i = ks * 8 + nb;
+          if ((slot_i & 1) && (slot_i >> 1) < kCopies) fire(gr, slot_i >> 1);
+        }
+      }
+      if constexpr (C::kKSteps * 4 < kCopies) {
+#pragma unroll
+        for (int i = C::kKSteps * 4; i < kCopies; ++i) fire(gr, i);
       }
     }
-    *(u32x4_t*)(a.k_out + (((int64_t)row0 + r) * H + h) * (kNope + kRope) + kNope + piece * 8) = o;
+    for (int s = C::kMfmaStages; s < S; ++s) {
+      {
+        const Group gr = stage_begin(s);
+#pragma unroll
+        for (int i = 0; i < kCopies; ++i) fire(gr, i);
+      }
+      // a rope slab (rope columns KC (s - kMfmaStages) .. +KC - 1): 256 rows of 4 logical pieces
+      // of 16 bytes, stored as bf16 (fp8: 8 output pieces per row, bf16: 4)
+      const KvbArgs& A = args();
+      const int H = A.num_heads;
+      const float scale = A.kv_scale;
+      KVB_LDS(uint8_t) ls = L + ((k * S + s) % C::kRing) * C::kStageBytes + C::kWSlabBytes;
+      constexpr int kOutPieces = FP8 ? 8 : 4;
+      const int col0 = kNope + C::KC * (s - C::kMfmaStages);
+#pragma unroll
+      for (int i = 0; i < kChunkRows * kOutPieces / 512; ++i) {
+        const int id = i * 512 + tid;
+        const int t = id / kOutPieces, piece = id % kOutPieces;
+        if (t >= cur.nrows) continue;
+        u32x4_t o;
+        if constexpr (FP8) {
+          const u32x2_t raw =
+              *(KVB_LDS(u32x2_t))(ls + t * kLatSlab + (((piece >> 1) ^ sw_lat(t)) << 4) + ((piece & 1) << 3));
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const unsigned lo = fp8x2_bf16x2<false>(raw[j]), hi = fp8x2_bf16x2<true>(raw[j]);
+            o[2 * j] = pack2(__uint_as_float(lo << 16) * scale, __uint_as_float(lo & 0xffff0000u) * scale);
+            o[2 * j + 1] = pack2(__uint_as_float(hi << 16) * scale, __uint_as_float(hi & 0xffff0000u) * scale);
+          }
+        } else {
+          o = *(KVB_LDS(u32x4_t))(ls + t * kLatSlab + ((piece ^ sw_lat(t)) << 4));
+        }
+        *(u32x4_t*)(A.k_out + ((int64_t)(cur.orow + t) * H + cur.h) * (kNope + kRope) + col0 + piece * 8) = o;
+      }
+      // with the last stage, the results (acc[2i + e][tb][v] is output column 32 i + 8 g + 4 e + v
+      // of chunk row th*64 + tb*16 + l16): a wave's next copy wait also waits for its stores to
+      // complete, so they go as late in the program as they can
+      if (s == S - 1) {
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          const int t = th * 64 + tb * 16 + l16;
+          if (t < cur.nrows) {
+            const int64_t o = (int64_t)(cur.orow + t) * H + cur.h;
+            uint16_t* dst = nh == 0 ? A.k_out + o * (kNope + kRope) : A.v_out + o * kVDim;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const f32x4_t x = acc[2 * i][tb], y = acc[2 * i + 1][tb];
+              *(u32x4_t*)(dst + i * 32 + g * 8) =
+                  u32x4_t{pack2(x[0] * scale, x[1] * scale), pack2(x[2] * scale, x[3] * scale),
+                          pack2(y[0] * scale, y[1] * scale), pack2(y[2] * scale, y[3] * scale)};
+            }
+          }
+        }
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) acc[nb][tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    // ---- next program (its record was written at stage kPageStages of the program before this one)
+    ++k;
+    cur = ring_get(k & 3);
   }
+  kvb_wait_vmcnt<0>();  // every copy of this wave has landed before the workgroup ends
+  if (wave == 0) {
+    uint32_t* status = args().status;
+    if (bits && status) atomicOr(status, bits);
+  }
+}
+
+// CUs of the current device, looked up once per device
+int kvb_num_cu() {
+  static std::mutex mu;
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 }  // namespace
@@ -279,8 +654,17 @@ extern "C" mla_status_t mla_gather_kv_b_proj(const mla_kv_b_proj_params_t* p, co
     return MLA_ERR_INVALID_ARG;
   const int64_t chunks = (p->max_context_len + mla::kChunkRows - 1) / mla::kChunkRows;
   const int64_t programs = (int64_t)p->batch * chunks * p->num_heads;
-  const int64_t grid = (programs + mla::kXcds - 1) / mla::kXcds * mla::kXcds;
-  if (grid > 0x7fffffff) return MLA_ERR_UNSUPPORTED;
+  if (programs > 0x7fffffff) return MLA_ERR_UNSUPPORTED;
+  const int num_cu = mla::kvb_num_cu();
+  if (num_cu < 1) return MLA_ERR_HIP;
+  // one workgroup per CU (a multiple of the XCD count), no more than there are programs
+  int64_t grid = std::max<int64_t>(num_cu / mla::kXcds, 1) * mla::kXcds;
+  grid = std::min<int64_t>(grid, (programs + mla::kXcds - 1) / mla::kXcds * mla::kXcds);
+  // heads in blocks of up to 4 (a divisor of H): the programs running together on one XCD
+  // cover a few heads of several chunks
+  int hb = 1;
+  for (int d = 1; d <= 4; ++d)
+    if (p->num_heads % d == 0) hb = d;
   mla::KvbArgs a;
   a.cache = static_cast<const uint8_t*>(d_kv_cache);
   a.kv_indptr = d_kv_indptr;
@@ -292,14 +676,16 @@ extern "C" mla_status_t mla_gather_kv_b_proj(const mla_kv_b_proj_params_t* p, co
   a.status = d_status;
   a.num_slots = p->num_slots;
   a.num_out_rows = p->num_out_rows;
-  a.programs = programs;
+  a.programs = (int32_t)programs;
   a.num_heads = p->num_heads;
   a.page_size = p->page_size;
   a.chunks = (int32_t)chunks;
   a.max_ctx = p->max_context_len;
+  a.head_block = hb;
+  a.page_magic = (uint32_t)(0xFFFFFFFFull / (uint64_t)p->page_size);
   a.kv_scale = p->kv_scale;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const dim3 g((unsigned)grid), blk(256);
+  const dim3 g((unsigned)grid), blk(512);
   if (p->kv_dtype == MLA_KV_FP8_E4M3FN) hipLaunchKernelGGL(mla::mla_kv_b_proj_kernel<true>, g, blk, 0, st, a);
   else hipLaunchKernelGGL(mla::mla_kv_b_proj_kernel<false>, g, blk, 0, st, a);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;

@@ -261,3 +261,13 @@ def test_kv_b_proj_nulls_and_empty_calls():
     assert mla.lib().mla_gather_kv_b_proj(mla.make_kv_b_proj_params(**dict(kw, batch=0)), *([None] * 9)) == 0
     assert mla.lib().mla_gather_kv_b_proj(mla.make_kv_b_proj_params(**dict(kw, max_context_len=0)),
                                           *([None] * 9)) == 0
+
+
+def test_kv_b_proj_rejects_more_programs_than_32_bits_count():
+    # 2^20 sequences x ceil(4096 / 256) = 16 chunks x 128 heads = 2^31 programs of 256 cached rows
+    # and one head: refused on the host, before any device work (the buffers are placeholders that
+    # are never touched)
+    kw = dict(batch=2 ** 20, num_heads=128, page_size=1, kv_dtype="bf16", kv_scale=1.0, max_context_len=4096,
+              num_slots=1000, num_out_rows=200)
+    fake = [ctypes.c_void_p(4096)] * 8 + [None]
+    assert mla.lib().mla_gather_kv_b_proj(mla.make_kv_b_proj_params(**kw), *fake) == 2

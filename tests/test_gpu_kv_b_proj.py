@@ -101,6 +101,23 @@ def test_ragged_workloads(name):
     compare(c, k, v, label=name)
 
 
+def test_many_empty_programs_per_workgroup():
+    # One long sequence sizes the chunk axis (300 chunks of 256 rows) for 64 sequences of one head:
+    # 19200 programs, about 75 per persistent workgroup, most of them past their sequence's end, so
+    # each workgroup's walk crosses its 64-program windows of sequence bounds while skipping.
+    rng = np.random.default_rng(2024)
+    ctx = [int(x) for x in rng.integers(1, 3000, size=64)]
+    ctx[37] = 300 * 256
+    pool = sum(-(-x // 16) for x in ctx) + 8
+    c = make_kvb_case(batch=64, num_heads=1, ctx=ctx, page_size=16, kv_dtype="fp8_e4m3fn", seed=77, pool_pages=pool)
+    k, v, status = run(c)
+    assert status == 0
+    rows = [(b, r) for b in (0, 1, 36, 38, 63) for r in range(ctx[b])]
+    rows += [(37, int(r)) for r in rng.choice(ctx[37], size=1500, replace=False)]
+    rows += [(37, r) for r in (0, 255, 256, ctx[37] - 1)]
+    compare(c, k, v, rows=rows, label="many empty programs")
+
+
 @pytest.mark.parametrize("name", ["kvb_b1_h12_ctx109440_fp8", "kvb_b1_h12_ctx65536_fp8", "kvb_b1_h12_ctx32000_fp8",
                                   "kvb_b1_h12_ctx4096_fp8"])
 def test_full_size_every_row(name):
