@@ -56,7 +56,9 @@ typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2_t;
 constexpr int kChunkRows = 256;                      // cached rows per program
 constexpr int kWRows = 256;                          // rows of W[h]: K nope, then V
 constexpr int kNope = 128, kVDim = 128, kRope = 64;  // K is 192 wide: nope then rope
-constexpr int kWaves = 8;
+constexpr int kWaves = 8;      // MFMA waves: the 256 x 256 output tile
+constexpr int kCopyWaves = 4;  // copy waves: every slab's copies and the bookkeeping
+constexpr int kThreads = (kWaves + kCopyWaves) * 64;
 constexpr int kXcds = 8;
 constexpr int kWindow = 64;     // programs whose sequence bounds one copy fetches
 constexpr int kLatSlab = 64;    // bytes of a latent row per stage (64 fp8 or 32 bf16 columns)
@@ -74,9 +76,9 @@ struct KvbCfg {
   static constexpr int kWSlabBytes = kWRows * kWRowBytes;    // 32 KB | 16 KB
   static constexpr int kWRowsPerInst = 1024 / kWRowBytes;    // 8 | 16
   static constexpr int kWInsts = kWSlabBytes / 1024;         // 32 | 16
-  static constexpr int kWPerWave = kWInsts / kWaves;         // 4 | 2
+  static constexpr int kWPerWave = kWInsts / kCopyWaves;     // 8 | 4
   static constexpr int kLatInsts = kChunkRows * kLatSlab / 1024;  // 16: row 16 j + lane / 4
-  static constexpr int kLatPerWave = kLatInsts / kWaves;          // 2
+  static constexpr int kLatPerWave = kLatInsts / kCopyWaves;      // 4
   static constexpr int kRing = FP8 ? 3 : 4;
   static constexpr int kStageBytes = kWSlabBytes + kChunkRows * kLatSlab;
   static constexpr int kPageOff = kRing * kStageBytes;           // one program's page-list window
@@ -84,9 +86,9 @@ struct KvbCfg {
   static constexpr int kWinOff = kSlotOff + 2 * kChunkRows * 4;  // two windows of sequence bounds
   static constexpr int kProgOff = kWinOff + 2 * 4 * kWindow * 4;  // four program records of 8 words
   static constexpr int kLdsBytes = kProgOff + 4 * 32;
-  // copies a wave issues with stage s of a program: its share of the W slab (MFMA stages), of the
-  // latent slab and, for wave 0 (cls 0) on the first stages, a quarter of the next program's
-  // page-list window
+  // copies a copy wave issues with stage s of a program: its share of the W slab (MFMA stages),
+  // of the latent slab and, for copy wave 0 (cls 0) on the first stages, a quarter of the next
+  // program's page-list window
   static constexpr int wave_insts(int cls, int s) {
     return (s < kMfmaStages ? kWPerWave : 0) + kLatPerWave + (s < kPageStages && cls == 0 ? 1 : 0);
   }
@@ -96,7 +98,7 @@ struct KvbCfg {
     for (int u = 1; u <= kRing - 2; ++u) n += wave_insts(cls, (s + u) % kStages);
     return n;
   }
-  static_assert(kWInsts % kWaves == 0 && kLatInsts % kWaves == 0, "copy shares");
+  static_assert(kWInsts % kCopyWaves == 0 && kLatInsts % kCopyWaves == 0, "copy shares");
   static_assert(kStages > kPageStages + kRing, "page-list window and slots are ready in time");
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
@@ -207,7 +209,7 @@ __device__ __forceinline__ void kvb_decode(const KvbArgs& a, int p, int& b, int&
 }
 
 template <bool FP8>
-__global__ __launch_bounds__(512) void mla_kv_b_proj_kernel(KvbArgs a) {
+__global__ __launch_bounds__(kThreads) void mla_kv_b_proj_kernel(KvbArgs a) {
   using C = KvbCfg<FP8>;
   constexpr int S = C::kStages;
   // The arguments are read from the kernarg segment where they are used, through a pointer
@@ -226,102 +228,9 @@ __global__ __launch_bounds__(512) void mla_kv_b_proj_kernel(KvbArgs a) {
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int l16 = lane & 15, g = lane >> 4;
-  const int nh = wave & 1, th = wave >> 1;
+  const bool copier = wave >= kWaves;
+  const int cw = wave - kWaves;  // copy wave index (copy waves only)
 
-  // this workgroup's programs: candidates m = 0 .. count - 1 are programs first + m * step
-  // (XCD-contiguous ranges: the workgroups of one XCD take adjacent programs)
-  auto cand_first = [&]() -> int {
-    const int range = (args().programs + kXcds - 1) / kXcds;
-    return (int)(blockIdx.x % kXcds) * range + (int)(blockIdx.x / kXcds);
-  };
-  const int step = gridDim.x / kXcds;
-  int count;
-  {
-    const int range = (a.programs + kXcds - 1) / kXcds;
-    const int xcd = blockIdx.x % kXcds;
-    const int first = xcd * range + (int)(blockIdx.x / kXcds);
-    const int end = min(a.programs, (xcd + 1) * range);
-    count = first < end ? (end - first + step - 1) / step : 0;
-  }
-
-  // ---------------------------------------------------------------- wave 0's bookkeeping
-  // Program records are found two programs ahead from windows of 64 candidates' sequence
-  // bounds that wave 0 copies into LDS; the page-list window of a program is copied with the
-  // first four stages of the program before it, and its row slots are worked out at that
-  // program's stage 4.
-  uint32_t bits = 0;  // status bits found by this lane (wave 0)
-  int cand = 0;       // next candidate to examine
-  int win_issued = -1, win_ready = -1;
-
-  auto issue_window = [&](int w) {  // sequence bounds of candidates 64 w .. 64 w + 63
-    const KvbArgs& A = args();
-    const int m = w * kWindow + lane;
-    const int32_t* s0 = A.cu_ctx;
-    const int32_t* s1 = A.cu_ctx;
-    const int32_t* s2 = A.cu_ctx;
-    const int32_t* s3 = A.cu_ctx;
-    if (m < count) {
-      int b, chunk, h;
-      kvb_decode(A, cand_first() + m * step, b, chunk, h);
-      s0 = A.cu_ctx + b;
-      s1 = A.cu_ctx + b + 1;
-      s2 = A.kv_indptr + b;
-      s3 = A.kv_indptr + b + 1;
-    }
-    const uint32_t dst = lds_base + C::kWinOff + (uint32_t)(w & 1) * (4 * kWindow * 4);
-    kvb_dma4(s0, dst);
-    kvb_dma4(s1, dst + 256);
-    kvb_dma4(s2, dst + 512);
-    kvb_dma4(s3, dst + 768);
-  };
-  // the next valid program from candidate `cand` on (all lanes take the same path)
-  auto find_next = [&]() -> KvbProg {
-    KvbProg r = {};
-    while (cand < count) {
-      const KvbArgs& A = args();
-      const int w = cand / kWindow;
-      if (w + 1 > win_issued && (w + 1) * kWindow < count) {
-        issue_window(w + 1);
-        win_issued = w + 1;
-      }
-      if (w > win_ready) {  // its copy may be in flight: wait for everything
-        kvb_wait_vmcnt<0>();
-        win_ready = win_issued;
-      }
-      KVB_LDS(int32_t) wb = (KVB_LDS(int32_t))(L + C::kWinOff + (w & 1) * (4 * kWindow * 4));
-      const int e = cand % kWindow;
-      const int32_t row0 = wb[e], row1 = wb[kWindow + e], pg0 = wb[2 * kWindow + e], pg1 = wb[3 * kWindow + e];
-      int b, chunk, h;
-      kvb_decode(A, cand_first() + cand * step, b, chunk, h);
-      ++cand;
-      const int ctx = row1 - row0;
-      if (row0 < 0 || ctx < 0 || (int64_t)row0 + ctx > A.num_out_rows) {  // rows outside the outputs
-        if (chunk == 0 && h == 0) bits |= MLA_KVB_ROWS_OUT_OF_RANGE;
-        continue;
-      }
-      if (chunk == 0 && h == 0 && ctx > A.max_ctx) bits |= MLA_KVB_CTX_TOO_LONG;  // rows past it not written
-      const int lim = min(ctx, A.max_ctx);
-      const int r0 = chunk * kChunkRows;
-      if (r0 >= lim) continue;  // past this sequence's last chunk
-      r = KvbProg{1, h, row0 + r0, min(kChunkRows, lim - r0), r0, max(pg0, 0), pg1, 0};
-      break;
-    }
-    return r;
-  };
-  auto publish = [&](const KvbProg& q, int slot) {  // program record -> LDS ring entry
-    if (lane == 0) {
-      KVB_LDS(int32_t) r = prog_ring + slot * 8;
-      r[0] = q.valid;
-      r[1] = q.h;
-      r[2] = q.orow;
-      r[3] = q.nrows;
-      r[4] = q.r0;
-      r[5] = q.pg_first;
-      r[6] = q.pg_end;
-      r[7] = q.bad;
-    }
-  };
   auto ring_get = [&](int slot) -> KvbProg {  // a program record, as scalars
     KVB_LDS(int32_t) r = prog_ring + slot * 8;
     return KvbProg{__builtin_amdgcn_readfirstlane(r[0]), __builtin_amdgcn_readfirstlane(r[1]),
@@ -329,250 +238,333 @@ __global__ __launch_bounds__(512) void mla_kv_b_proj_kernel(KvbArgs a) {
                    __builtin_amdgcn_readfirstlane(r[4]), __builtin_amdgcn_readfirstlane(r[5]),
                    __builtin_amdgcn_readfirstlane(r[6]), __builtin_amdgcn_readfirstlane(r[7])};
   };
-  // page-list window copy j (ids 64 j .. 64 j + 63) of program q
-  auto issue_pages = [&](const KvbProg& q, int j) {
-    const KvbArgs& A = args();
-    const int32_t* src = A.cu_ctx;  // a harmless valid word when the id is not needed
-    if (q.valid) {
-      const int64_t gi = (int64_t)q.pg_first + kvb_page_div(q.r0, A) + j * 64 + lane;
-      if (gi < q.pg_end) src = A.kv_page_indices + gi;
+
+  if (copier) {
+    // ============================================================ copy waves
+    // this workgroup's programs: candidates m = 0 .. count - 1 are programs first + m * step
+    // (XCD-contiguous ranges: the workgroups of one XCD take adjacent programs)
+    auto cand_first = [&]() -> int {
+      const int range = (args().programs + kXcds - 1) / kXcds;
+      return (int)(blockIdx.x % kXcds) * range + (int)(blockIdx.x / kXcds);
+    };
+    const int step = gridDim.x / kXcds;
+    int count;
+    {
+      const int range = (a.programs + kXcds - 1) / kXcds;
+      const int xcd = blockIdx.x % kXcds;
+      const int first = xcd * range + (int)(blockIdx.x / kXcds);
+      const int end = min(a.programs, (xcd + 1) * range);
+      count = first < end ? (end - first + step - 1) / step : 0;
     }
-    kvb_dma4(src, lds_base + C::kPageOff + (uint32_t)j * 256);
-  };
-  // row slots of program q (ring entry `slot`) from its page-list window, 4 rows per lane of
-  // wave 0; records in the entry whether any row has no valid slot
-  auto make_slots = [&](int slot, int parity) {
-    const KvbProg q = ring_get(slot);
-    KVB_LDS(int32_t) pt = (KVB_LDS(int32_t))(L + C::kPageOff);
-    KVB_LDS(int32_t) st = (KVB_LDS(int32_t))(L + C::kSlotOff) + parity * kChunkRows;
-    const KvbArgs& A = args();
-    const int P = A.page_size;
-    const int npages = q.pg_end - q.pg_first;
-    const int page0 = kvb_page_div(q.r0, A);
-    bool any = false;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = lane + 64 * i;
-      const int ra = q.r0 + min(r, q.nrows - 1);
-      const int page = kvb_page_div(ra, A);
-      int32_t sl = -1;
-      if (page < npages) {
-        const int64_t v = (int64_t)pt[page - page0] * P + (ra - page * P);
-        if (v >= 0 && v < A.num_slots) sl = (int32_t)v;
-        else if (r < q.nrows) bits |= MLA_KVB_SLOT_OUT_OF_RANGE;
-      } else if (r < q.nrows) {
-        bits |= MLA_KVB_TOO_FEW_PAGES;
+
+    // ---- copy wave 0's bookkeeping. Program records are found two programs ahead from
+    // windows of 64 candidates' sequence bounds copied into LDS; the page-list window of a
+    // program is copied with the first four stages of the program before it, and its row
+    // slots are worked out at that program's stage 4.
+    uint32_t bits = 0;  // status bits found by this lane (copy wave 0)
+    int cand = 0;       // next candidate to examine
+    int win_issued = -1, win_ready = -1;
+
+    auto issue_window = [&](int w) {  // sequence bounds of candidates 64 w .. 64 w + 63
+      const KvbArgs& A = args();
+      const int m = w * kWindow + lane;
+      const int32_t* s0 = A.cu_ctx;
+      const int32_t* s1 = A.cu_ctx;
+      const int32_t* s2 = A.cu_ctx;
+      const int32_t* s3 = A.cu_ctx;
+      if (m < count) {
+        int b, chunk, h;
+        kvb_decode(A, cand_first() + m * step, b, chunk, h);
+        s0 = A.cu_ctx + b;
+        s1 = A.cu_ctx + b + 1;
+        s2 = A.kv_indptr + b;
+        s3 = A.kv_indptr + b + 1;
       }
-      any |= sl < 0;
-      st[r] = sl;
-    }
-    const bool bad = __builtin_amdgcn_ballot_w64(any) != 0;  // over all 64 lanes, before the lane-0 store
-    if (lane == 0) prog_ring[slot * 8 + 7] = bad;
-  };
-
-  // ---------------------------------------------------------------- every wave's copies
-  // W copy j: row kWRowsPerInst j + lane / (64 / kWRowsPerInst), place lane % (64 / kWRowsPerInst),
-  // holding logical piece place ^ sw_w(row); this wave's are j = kWPerWave wave + i. Latent copy
-  // j: row 16 j + lane / 4, place lane % 4 holding logical piece place ^ sw_lat(row) (the same
-  // for every j: sw_lat(16 j + lane / 4) = (lane >> 4) & 3); this wave's are j = 2 wave, 2 wave + 1.
-  constexpr int kWLanesPerRow = 64 / C::kWRowsPerInst;  // 8 | 4
-  uint32_t w_off[C::kWPerWave];
+      const uint32_t dst = lds_base + C::kWinOff + (uint32_t)(w & 1) * (4 * kWindow * 4);
+      kvb_dma4(s0, dst);
+      kvb_dma4(s1, dst + 256);
+      kvb_dma4(s2, dst + 512);
+      kvb_dma4(s3, dst + 768);
+    };
+    // the next valid program from candidate `cand` on (all lanes take the same path)
+    auto find_next = [&]() -> KvbProg {
+      KvbProg r = {};
+      while (cand < count) {
+        const KvbArgs& A = args();
+        const int w = cand / kWindow;
+        if (w + 1 > win_issued && (w + 1) * kWindow < count) {
+          issue_window(w + 1);
+          win_issued = w + 1;
+        }
+        if (w > win_ready) {  // its copy may be in flight: wait for everything
+          kvb_wait_vmcnt<0>();
+          win_ready = win_issued;
+        }
+        KVB_LDS(int32_t) wb = (KVB_LDS(int32_t))(L + C::kWinOff + (w & 1) * (4 * kWindow * 4));
+        const int e = cand % kWindow;
+        const int32_t row0 = wb[e], row1 = wb[kWindow + e], pg0 = wb[2 * kWindow + e], pg1 = wb[3 * kWindow + e];
+        int b, chunk, h;
+        kvb_decode(A, cand_first() + cand * step, b, chunk, h);
+        ++cand;
+        const int ctx = row1 - row0;
+        if (row0 < 0 || ctx < 0 || (int64_t)row0 + ctx > A.num_out_rows) {  // rows outside the outputs
+          if (chunk == 0 && h == 0) bits |= MLA_KVB_ROWS_OUT_OF_RANGE;
+          continue;
+        }
+        if (chunk == 0 && h == 0 && ctx > A.max_ctx) bits |= MLA_KVB_CTX_TOO_LONG;  // rows past it not written
+        const int lim = min(ctx, A.max_ctx);
+        const int r0 = chunk * kChunkRows;
+        if (r0 >= lim) continue;  // past this sequence's last chunk
+        r = KvbProg{1, h, row0 + r0, min(kChunkRows, lim - r0), r0, max(pg0, 0), pg1, 0};
+        break;
+      }
+      return r;
+    };
+    auto publish = [&](const KvbProg& q, int slot) {  // program record -> LDS ring entry
+      if (lane == 0) {
+        KVB_LDS(int32_t) r = prog_ring + slot * 8;
+        r[0] = q.valid;
+        r[1] = q.h;
+        r[2] = q.orow;
+        r[3] = q.nrows;
+        r[4] = q.r0;
+        r[5] = q.pg_first;
+        r[6] = q.pg_end;
+        r[7] = q.bad;
+      }
+    };
+    // page-list window copy j (ids 64 j .. 64 j + 63) of program q
+    auto issue_pages = [&](const KvbProg& q, int j) {
+      const KvbArgs& A = args();
+      const int32_t* src = A.cu_ctx;  // a harmless valid word when the id is not needed
+      if (q.valid) {
+        const int64_t gi = (int64_t)q.pg_first + kvb_page_div(q.r0, A) + j * 64 + lane;
+        if (gi < q.pg_end) src = A.kv_page_indices + gi;
+      }
+      kvb_dma4(src, lds_base + C::kPageOff + (uint32_t)j * 256);
+    };
+    // row slots of program q (ring entry `slot`) from its page-list window, 4 rows per lane;
+    // records in the entry whether any row has no valid slot
+    auto make_slots = [&](int slot, int parity) {
+      const KvbProg q = ring_get(slot);
+      KVB_LDS(int32_t) pt = (KVB_LDS(int32_t))(L + C::kPageOff);
+      KVB_LDS(int32_t) st = (KVB_LDS(int32_t))(L + C::kSlotOff) + parity * kChunkRows;
+      const KvbArgs& A = args();
+      const int P = A.page_size;
+      const int npages = q.pg_end - q.pg_first;
+      const int page0 = kvb_page_div(q.r0, A);
+      bool any = false;
 #pragma unroll
-  for (int i = 0; i < C::kWPerWave; ++i) {
-    const int j = C::kWPerWave * wave + i;
-    const int row = C::kWRowsPerInst * j + lane / kWLanesPerRow;
-    const int place = lane % kWLanesPerRow;
-    w_off[i] = (uint32_t)(row * (kLatentDim * 2) + ((place ^ sw_w<FP8>(row)) << 4));
+      for (int i = 0; i < 4; ++i) {
+        const int r = lane + 64 * i;
+        const int ra = q.r0 + min(r, q.nrows - 1);
+        const int page = kvb_page_div(ra, A);
+        int32_t sl = -1;
+        if (page < npages) {
+          const int64_t v = (int64_t)pt[page - page0] * P + (ra - page * P);
+          if (v >= 0 && v < A.num_slots) sl = (int32_t)v;
+          else if (r < q.nrows) bits |= MLA_KVB_SLOT_OUT_OF_RANGE;
+        } else if (r < q.nrows) {
+          bits |= MLA_KVB_TOO_FEW_PAGES;
+        }
+        any |= sl < 0;
+        st[r] = sl;
+      }
+      const bool bad = __builtin_amdgcn_ballot_w64(any) != 0;  // over all 64 lanes, before the lane-0 store
+      if (lane == 0) prog_ring[slot * 8 + 7] = bad;
+    };
+
+    // ---- the copies. W copy j: row kWRowsPerInst j + lane / (64 / kWRowsPerInst), place
+    // lane % (64 / kWRowsPerInst), holding logical piece place ^ sw_w(row); this wave's are
+    // j = kWPerWave cw + i. Latent copy j: row 16 j + lane / 4, place lane % 4 holding logical
+    // piece place ^ sw_lat(row) (the same for every j: (lane & 3) ^ ((lane >> 4) & 3)); this
+    // wave's are j = kLatPerWave cw + i.
+    constexpr int kWLanesPerRow = 64 / C::kWRowsPerInst;  // 8 | 4
+    uint32_t w_off[C::kWPerWave];
+#pragma unroll
+    for (int i = 0; i < C::kWPerWave; ++i) {
+      const int j = C::kWPerWave * cw + i;
+      const int row = C::kWRowsPerInst * j + lane / kWLanesPerRow;
+      const int place = lane % kWLanesPerRow;
+      w_off[i] = (uint32_t)(row * (kLatentDim * 2) + ((place ^ sw_w<FP8>(row)) << 4));
+    }
+    const int lat_logical = (lane & 3) ^ ((lane >> 4) & 3);
+    // this wave's copies of stage s of program k (record in ring entry k & 3, slots in table
+    // k & 1) and, for copy wave 0 on the first stages, a quarter of program k + 1's page-list window
+    auto issue_group = [&](int k, int s) {
+      const KvbArgs& A = args();
+      const uint32_t stage = lds_base + (uint32_t)(((k * S + s) % C::kRing) * C::kStageBytes);
+      if (s < C::kMfmaStages) {
+        const int32_t qh = __builtin_amdgcn_readfirstlane(prog_ring[(k & 3) * 8 + 1]);
+        const uint8_t* wsrc = (const uint8_t*)(A.w + (int64_t)qh * kWRows * kLatentDim) + s * C::kWRowBytes;
+#pragma unroll
+        for (int i = 0; i < C::kWPerWave; ++i)
+          kvb_dma16s(wsrc, w_off[i], stage + (uint32_t)(C::kWPerWave * cw + i) * 1024);
+      }
+      KVB_LDS(int32_t) st = (KVB_LDS(int32_t))(L + C::kSlotOff) + (k & 1) * kChunkRows;
+#pragma unroll
+      for (int i = 0; i < C::kLatPerWave; ++i) {
+        const int j = C::kLatPerWave * cw + i;
+        const int32_t sl = max(st[16 * j + (lane >> 2)], 0);
+        kvb_dma16(A.cache + (int64_t)sl * C::kRowBytes + s * kLatSlab + lat_logical * 16,
+                  stage + (uint32_t)(C::kWSlabBytes + j * 1024));
+      }
+      if (s < kPageStages && cw == 0) issue_pages(ring_get((k + 1) & 3), s);
+    };
+    // after this wave's stage-s copies of program k have landed: zero the latent pieces of rows
+    // with no valid slot
+    auto zero_bad = [&](int k, int s) {
+      KVB_LDS(int32_t) st = (KVB_LDS(int32_t))(L + C::kSlotOff) + (k & 1) * kChunkRows;
+      KVB_LDS(uint8_t) lat = L + ((k * S + s) % C::kRing) * C::kStageBytes + C::kWSlabBytes;
+#pragma unroll
+      for (int i = 0; i < C::kLatPerWave; ++i) {
+        const int j = C::kLatPerWave * cw + i;
+        if (st[16 * j + (lane >> 2)] < 0) *(KVB_LDS(u32x4_t))(lat + j * 1024 + lane * 16) = u32x4_t{0, 0, 0, 0};
+      }
+    };
+
+    // ---- prologue
+    if (cw == 0) {
+      if (count > 0) {
+        issue_window(0);
+        win_issued = 0;
+        kvb_wait_vmcnt<0>();
+        win_ready = 0;
+      }
+      const KvbProg p0 = find_next();
+      const KvbProg p1 = p0.valid ? find_next() : KvbProg{};
+      publish(p0, 0);
+      publish(p1, 1);
+      publish(KvbProg{}, 2);
+      if (p0.valid) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) issue_pages(p0, j);
+        kvb_wait_vmcnt<0>();
+        win_ready = win_issued;
+        make_slots(0, 0);
+      }
+    }
+    __syncthreads();
+    KvbProg cur = ring_get(0);
+    if (cur.valid) {
+      // stages 0 .. kRing - 2 of program 0 (the first ones carry program 1's page-list window)
+#pragma unroll
+      for (int s = 0; s < C::kRing - 1; ++s) issue_group(0, s);
+    }
+    for (int k = 0; cur.valid; ++k) {
+      const bool next_valid = __builtin_amdgcn_readfirstlane(prog_ring[((k + 1) & 3) * 8]) != 0;
+#pragma unroll 1
+      for (int s = 0; s < S; ++s) {
+        // this wave's stage-s copies have landed once its younger copies are all that may be in flight
+        if (s + C::kRing - 2 >= S && !next_valid) kvb_wait_vmcnt<0>();
+        else if (cw == 0) kvb_wait_stage<C, 0>(s);
+        else kvb_wait_stage<C, 1>(s);
+        if (cur.bad) zero_bad(k, s);
+        __syncthreads();  // stage s is in LDS for every wave; every wave is done with stage s - 1
+        if (cw == 0 && s == kPageStages && next_valid) make_slots((k + 1) & 3, (k + 1) & 1);  // program k + 1
+        if (cw == 0 && s == kPageStages + 1) publish(next_valid ? find_next() : KvbProg{}, (k + 2) & 3);
+        // this wave's copies of stage s + kRing - 1 (this program's or the next one's), into the
+        // slot of stage s - 1, which every wave is done with
+        const int t = s + C::kRing - 1;
+        if (t < S) issue_group(k, t);
+        else if (next_valid) issue_group(k + 1, t - S);
+      }
+      cur = ring_get((k + 1) & 3);  // written at stage kPageStages + 1 of the program before this one
+    }
+    kvb_wait_vmcnt<0>();  // every copy of this wave has landed before the workgroup ends
+    if (cw == 0) {
+      uint32_t* status = args().status;
+      if (bits && status) atomicOr(status, bits);
+    }
+    return;
   }
-  const int lat_logical = (lane & 3) ^ ((lane >> 4) & 3);
 
-  // This wave's copies of stage s of program k (record in ring entry k & 3, slots in table
-  // k & 1) and, for wave 0 on the first stages, a quarter of program k + 1's page-list window:
-  // copy i < kWPerWave is a W piece (MFMA stages only), then kLatPerWave latent pieces, then the
-  // page-list piece. A stage's copies are issued one at a time between its MFMAs.
-  constexpr int kCopies = C::kWPerWave + C::kLatPerWave + 1;
-  struct Group {
-    bool on;                 // the stage exists
-    int s, k;
-    const uint8_t* wsrc;     // W slab base (scalar)
-    uint32_t stage;          // LDS stage base
-    const uint8_t* lat[C::kLatPerWave];
-  };
-  auto plan_group = [&](int k, int s, bool on) -> Group {
-    Group gr;
-    gr.on = on;
-    gr.s = s;
-    gr.k = k;
-    const KvbArgs& A = args();
-    gr.stage = lds_base + (uint32_t)(((k * S + s) % C::kRing) * C::kStageBytes);
-    const int32_t qh = __builtin_amdgcn_readfirstlane(prog_ring[(k & 3) * 8 + 1]);
-    gr.wsrc = (const uint8_t*)(A.w + (int64_t)qh * kWRows * kLatentDim) + s * C::kWRowBytes;
-    KVB_LDS(int32_t) st = (KVB_LDS(int32_t))(L + C::kSlotOff) + (k & 1) * kChunkRows;
+  // ============================================================ MFMA waves
+  // They issue no copy and wait on no memory counter: they read the published stages,
+  // multiply, and store (from registers; the stores complete on their own).
+  const int l16 = lane & 15, g = lane >> 4;
+  const int nh = wave & 1, th = wave >> 1;
+  // LDS byte offsets of the operand reads within a stage, per k-step. Every swizzle involved
+  // depends on the lane only: W row nh*128 + 32 (nb / 2) + 8 (l16 / 4) + 4 (nb % 2) + l16 % 4 has
+  // sw_w = sw_w(8 (l16 / 4) + l16 % 4), latent row th*64 + 16 tb + l16 has sw_lat = sw_lat(l16), so
+  // tile nb and tb only add compile-time row offsets. Opaque, so that the compiler keeps one
+  // register per k-step rather than one per tile.
+  const int w_row_lane = ((l16 >> 2) << 3) + (l16 & 3);
+  uint32_t w_lane[C::kKSteps], l_lane[C::kKSteps];
 #pragma unroll
-    for (int i = 0; i < C::kLatPerWave; ++i) {
-      const int j = C::kLatPerWave * wave + i;
-      const int32_t sl = max(st[16 * j + (lane >> 2)], 0);
-      gr.lat[i] = A.cache + (int64_t)sl * C::kRowBytes + s * kLatSlab + lat_logical * 16;
-    }
-    return gr;
-  };
-  auto fire = [&](const Group& gr, int i) {
-    if (!gr.on) return;
-    if (i < C::kWPerWave) {
-      if (gr.s < C::kMfmaStages) kvb_dma16s(gr.wsrc, w_off[i], gr.stage + (uint32_t)(C::kWPerWave * wave + i) * 1024);
-    } else if (i < C::kWPerWave + C::kLatPerWave) {
-      const int j = C::kLatPerWave * wave + (i - C::kWPerWave);
-      kvb_dma16(gr.lat[i - C::kWPerWave], gr.stage + (uint32_t)(C::kWSlabBytes + j * 1024));
-    } else if (gr.s < kPageStages && wave == 0) {
-      issue_pages(ring_get((gr.k + 1) & 3), gr.s);
-    }
-  };
-  auto issue_group = [&](int k, int s) {
-    const Group gr = plan_group(k, s, true);
-#pragma unroll
-    for (int i = 0; i < kCopies; ++i) fire(gr, i);
-  };
-  // after this wave's stage-s copies of program k have landed: zero the latent pieces of rows
-  // with no valid slot
-  auto zero_bad = [&](int k, int s) {
-    KVB_LDS(int32_t) st = (KVB_LDS(int32_t))(L + C::kSlotOff) + (k & 1) * kChunkRows;
-    KVB_LDS(uint8_t) lat = L + ((k * S + s) % C::kRing) * C::kStageBytes + C::kWSlabBytes;
-#pragma unroll
-    for (int i = 0; i < C::kLatPerWave; ++i) {
-      const int j = C::kLatPerWave * wave + i;
-      if (st[16 * j + (lane >> 2)] < 0) *(KVB_LDS(u32x4_t))(lat + j * 1024 + lane * 16) = u32x4_t{0, 0, 0, 0};
-    }
-  };
-  auto wait_stage = [&](int s, bool full) {  // full: the younger stages were all issued
-    if (!full) kvb_wait_vmcnt<0>();
-    else if (wave == 0) kvb_wait_stage<C, 0>(s);
-    else kvb_wait_stage<C, 1>(s);
-  };
-
-  // ---------------------------------------------------------------- prologue
-  if (wave == 0) {
-    if (count > 0) {
-      issue_window(0);
-      win_issued = 0;
-      kvb_wait_vmcnt<0>();
-      win_ready = 0;
-    }
-    const KvbProg p0 = find_next();
-    const KvbProg p1 = p0.valid ? find_next() : KvbProg{};
-    publish(p0, 0);
-    publish(p1, 1);
-    publish(KvbProg{}, 2);
-    if (p0.valid) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) issue_pages(p0, j);
-      kvb_wait_vmcnt<0>();
-      win_ready = win_issued;
-      make_slots(0, 0);
-    }
+  for (int ks = 0; ks < C::kKSteps; ++ks) {
+    w_lane[ks] = (uint32_t)((nh * 128 + w_row_lane) * C::kWRowBytes + (((4 * ks + g) ^ sw_w<FP8>(w_row_lane)) << 4));
+    if constexpr (FP8)
+      l_lane[ks] = (uint32_t)(C::kWSlabBytes + (th * 64 + l16) * kLatSlab + (((2 * ks + (g >> 1)) ^ sw_lat(l16)) << 4) +
+                              ((g & 1) << 3));
+    else
+      l_lane[ks] = (uint32_t)(C::kWSlabBytes + (th * 64 + l16) * kLatSlab + ((g ^ sw_lat(l16)) << 4));
+    asm volatile("" : "+v"(w_lane[ks]), "+v"(l_lane[ks]));
   }
-  __syncthreads();
-  KvbProg cur = ring_get(0);  // the program being computed
-  if (cur.valid) {
-    // stages 0 .. kRing - 2 of program 0 (the first ones carry program 1's page-list window)
-#pragma unroll
-    for (int s = 0; s < C::kRing - 1; ++s) issue_group(0, s);
-  }
-
+  __syncthreads();  // the prologue's program records
+  KvbProg cur = ring_get(0);
   f32x4_t acc[8][4];
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) acc[nb][tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  int k = 0;
-  bool next_valid = false;
-  // entering stage s of program k: this wave's stage-s copies have landed once its younger
-  // copies are all that may be in flight; the barrier publishes the stage to every wave (and
-  // every wave is then done with stage s - 1, whose slot the copies issued here refill)
-  auto stage_begin = [&](int s) -> Group {
-    wait_stage(s, s + C::kRing - 2 < S || next_valid);
-    if (cur.bad) zero_bad(k, s);
-    __syncthreads();
-    if (wave == 0 && s == kPageStages) {
-      // program k + 1's page-list window landed with the first stages: its row slots
-      if (next_valid) make_slots((k + 1) & 3, (k + 1) & 1);
-    }
-    if (wave == 0 && s == kPageStages + 1) {
-      // program k + 2 (its page-list window rides on program k + 1's first stages)
-      publish(next_valid ? find_next() : KvbProg{}, (k + 2) & 3);
-    }
-    // this wave's copies of stage t (this program's or the next one's)
-    const int t = s + C::kRing - 1;
-    return t < S ? plan_group(k, t, true) : plan_group(k + 1, t - S, next_valid);
-  };
-  while (cur.valid) {
-    // whether a program follows (its record was written two programs ago)
-    next_valid = __builtin_amdgcn_readfirstlane(prog_ring[((k + 1) & 3) * 8]) != 0;
+  for (int k = 0; cur.valid; ++k) {
+#pragma unroll 1
     for (int s = 0; s < C::kMfmaStages; ++s) {
-      const Group gr = stage_begin(s);
-      // the stage's MFMAs: W rows nh*128 + perm(nb, l16), chunk rows th*64 + tb*16 + l16,
-      // k piece 4 ks + g of the stage's columns
-      KVB_LDS(uint8_t) ws = L + ((k * S + s) % C::kRing) * C::kStageBytes;
-      KVB_LDS(uint8_t) ls = ws + C::kWSlabBytes;
+      __syncthreads();  // stage s is in LDS; every wave is done with stage s - 1
+      KVB_LDS(uint8_t) st = L + ((k * S + s) % C::kRing) * C::kStageBytes;
 #pragma unroll
       for (int ks = 0; ks < C::kKSteps; ++ks) {
         bf16x8_t bt[4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
-          const int row = th * 64 + tb * 16 + l16;
+          KVB_LDS(uint8_t) lp = st + l_lane[ks] + tb * 16 * kLatSlab;
           if constexpr (FP8) {
-            const u32x2_t raw = *(KVB_LDS(u32x2_t))(ls + row * kLatSlab + (((2 * ks + (g >> 1)) ^ sw_lat(row)) << 4) +
-                                                     ((g & 1) << 3));
+            const u32x2_t raw = *(KVB_LDS(u32x2_t))lp;
             const u32x4_t v = {fp8x2_bf16x2<false>(raw[0]), fp8x2_bf16x2<true>(raw[0]), fp8x2_bf16x2<false>(raw[1]),
                                fp8x2_bf16x2<true>(raw[1])};
             bt[tb] = __builtin_bit_cast(bf16x8_t, v);
           } else {
-            bt[tb] = *(KVB_LDS(bf16x8_t))(ls + row * kLatSlab + ((g ^ sw_lat(row)) << 4));
+            bt[tb] = *(KVB_LDS(bf16x8_t))lp;
           }
         }
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) {
           // tile nb's row m holds W row 32 (nb / 2) + 8 (m / 4) + 4 (nb % 2) + m % 4, so that a
           // lane's results of tiles 2i and 2i + 1 are 8 consecutive output columns
-          const int wrow = nh * 128 + (nb >> 1) * 32 + ((l16 >> 2) << 3) + ((nb & 1) << 2) + (l16 & 3);
           const bf16x8_t at =
-              *(KVB_LDS(bf16x8_t))(ws + wrow * C::kWRowBytes + (((4 * ks + g) ^ sw_w<FP8>(wrow)) << 4));
+              *(KVB_LDS(bf16x8_t))(st + w_lane[ks] + ((nb >> 1) * 32 + (nb & 1) * 4) * C::kWRowBytes);
 #pragma unroll
           for (int tb = 0; tb < 4; ++tb)
             acc[nb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(at, bt[tb], acc[nb][tb], 0, 0, 0);
-          // the stage's copies, one after every other tile row of MFMAs
-          const int slot_i = ks * 8 + nb;
-          if ((slot_i & 1) && (slot_i >> 1) < kCopies) fire(gr, slot_i >> 1);
         }
       }
-      if constexpr (C::kKSteps * 4 < kCopies) {
-#pragma unroll
-        for (int i = C::kKSteps * 4; i < kCopies; ++i) fire(gr, i);
-      }
     }
+#pragma unroll 1
     for (int s = C::kMfmaStages; s < S; ++s) {
-      {
-        const Group gr = stage_begin(s);
-#pragma unroll
-        for (int i = 0; i < kCopies; ++i) fire(gr, i);
-      }
+      __syncthreads();  // stage s is in LDS; every wave is done with stage s - 1
       // a rope slab (rope columns KC (s - kMfmaStages) .. +KC - 1): 256 rows of 4 logical pieces
-      // of 16 bytes, stored as bf16 (fp8: 8 output pieces per row, bf16: 4)
+      // of 16 bytes, stored as bf16 (fp8: 8 output pieces per row, bf16: 4). Thread id handles
+      // rows 512 i / kOutPieces + id / kOutPieces: the swizzle of its rows is the same for every i.
       const KvbArgs& A = args();
       const int H = A.num_heads;
       const float scale = A.kv_scale;
       KVB_LDS(uint8_t) ls = L + ((k * S + s) % C::kRing) * C::kStageBytes + C::kWSlabBytes;
       constexpr int kOutPieces = FP8 ? 8 : 4;
+      constexpr int kRowsPerPass = kWaves * 64 / kOutPieces;  // 64 | 128
       const int col0 = kNope + C::KC * (s - C::kMfmaStages);
+      int id = tid;
+      asm volatile("" : "+v"(id));
+      const int t0 = id / kOutPieces, piece = id % kOutPieces;
+      const uint32_t rope_lane = FP8 ? (uint32_t)(t0 * kLatSlab + (((piece >> 1) ^ sw_lat(t0)) << 4) + ((piece & 1) << 3))
+                                     : (uint32_t)(t0 * kLatSlab + ((piece ^ sw_lat(t0)) << 4));
 #pragma unroll
-      for (int i = 0; i < kChunkRows * kOutPieces / 512; ++i) {
-        const int id = i * 512 + tid;
-        const int t = id / kOutPieces, piece = id % kOutPieces;
+      for (int i = 0; i < kChunkRows / kRowsPerPass; ++i) {
+        const int t = t0 + i * kRowsPerPass;
         if (t >= cur.nrows) continue;
         u32x4_t o;
         if constexpr (FP8) {
-          const u32x2_t raw =
-              *(KVB_LDS(u32x2_t))(ls + t * kLatSlab + (((piece >> 1) ^ sw_lat(t)) << 4) + ((piece & 1) << 3));
+          const u32x2_t raw = *(KVB_LDS(u32x2_t))(ls + rope_lane + i * kRowsPerPass * kLatSlab);
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             const unsigned lo = fp8x2_bf16x2<false>(raw[j]), hi = fp8x2_bf16x2<true>(raw[j]);
@@ -580,14 +572,13 @@ __global__ __launch_bounds__(512) void mla_kv_b_proj_kernel(KvbArgs a) {
             o[2 * j + 1] = pack2(__uint_as_float(hi << 16) * scale, __uint_as_float(hi & 0xffff0000u) * scale);
           }
         } else {
-          o = *(KVB_LDS(u32x4_t))(ls + t * kLatSlab + ((piece ^ sw_lat(t)) << 4));
+          o = *(KVB_LDS(u32x4_t))(ls + rope_lane + i * kRowsPerPass * kLatSlab);
         }
         *(u32x4_t*)(A.k_out + ((int64_t)(cur.orow + t) * H + cur.h) * (kNope + kRope) + col0 + piece * 8) = o;
       }
-      // with the last stage, the results (acc[2i + e][tb][v] is output column 32 i + 8 g + 4 e + v
-      // of chunk row th*64 + tb*16 + l16): a wave's next copy wait also waits for its stores to
-      // complete, so they go as late in the program as they can
       if (s == S - 1) {
+        // the results (acc[2i + e][tb][v] is output column 32 i + 8 g + 4 e + v of chunk row
+        // th*64 + tb*16 + l16)
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
           const int t = th * 64 + tb * 16 + l16;
@@ -609,14 +600,7 @@ __global__ __launch_bounds__(512) void mla_kv_b_proj_kernel(KvbArgs a) {
           for (int tb = 0; tb < 4; ++tb) acc[nb][tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
     }
-    // ---- next program (its record was written at stage kPageStages of the program before this one)
-    ++k;
-    cur = ring_get(k & 3);
-  }
-  kvb_wait_vmcnt<0>();  // every copy of this wave has landed before the workgroup ends
-  if (wave == 0) {
-    uint32_t* status = args().status;
-    if (bits && status) atomicOr(status, bits);
+    cur = ring_get((k + 1) & 3);  // written at stage kPageStages + 1 of the program before this one
   }
 }
 
@@ -685,7 +669,7 @@ extern "C" mla_status_t mla_gather_kv_b_proj(const mla_kv_b_proj_params_t* p, co
   a.page_magic = (uint32_t)(0xFFFFFFFFull / (uint64_t)p->page_size);
   a.kv_scale = p->kv_scale;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const dim3 g((unsigned)grid), blk(512);
+  const dim3 g((unsigned)grid), blk(mla::kThreads);
   if (p->kv_dtype == MLA_KV_FP8_E4M3FN) hipLaunchKernelGGL(mla::mla_kv_b_proj_kernel<true>, g, blk, 0, st, a);
   else hipLaunchKernelGGL(mla::mla_kv_b_proj_kernel<false>, g, blk, 0, st, a);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
