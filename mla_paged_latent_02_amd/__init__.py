@@ -49,6 +49,11 @@ EXPORTED = ["mla_abi_version", "mla_status_string", "mla_plan_options_default", 
 INSERT_SLOT_OUT_OF_RANGE = 1
 INSERT_POSITION_OUT_OF_RANGE = 2
 
+KVB_TOO_FEW_PAGES = 1
+KVB_SLOT_OUT_OF_RANGE = 2
+KVB_ROWS_OUT_OF_RANGE = 4
+KVB_CTX_TOO_LONG = 8
+
 
 class DecodeParams(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seqlen_qo", ctypes.c_int32), ("num_heads", ctypes.c_int32),

@@ -271,3 +271,17 @@ def test_kv_b_proj_rejects_more_programs_than_32_bits_count():
               num_slots=1000, num_out_rows=200)
     fake = [ctypes.c_void_p(4096)] * 8 + [None]
     assert mla.lib().mla_gather_kv_b_proj(mla.make_kv_b_proj_params(**kw), *fake) == 2
+
+
+def test_status_bits_of_the_header_match_the_binding():
+    # every status bit the header defines (decode device bits, stale plan included; epilogue; expansion)
+    # has a binding constant of the same value, and the bits of each group are distinct powers of two
+    text = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                             "mla_decode.h")).read()
+    defs = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define MLA_((?:DEV|INSERT|KVB)_\w+) (\d+)u", text)}
+    assert "DEV_STALE_PLAN" in defs and len(defs) >= 11
+    for name, value in defs.items():
+        assert getattr(mla, name) == value, name
+    for group in ("DEV_", "INSERT_", "KVB_"):
+        vals = [v for k, v in defs.items() if k.startswith(group)]
+        assert all(v & (v - 1) == 0 for v in vals) and len(set(vals)) == len(vals), group
