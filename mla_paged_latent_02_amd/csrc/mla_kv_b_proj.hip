@@ -7,12 +7,16 @@
 // (128 K-nope then 128 V) on bf16 MFMA (16x16x32), and the 64 rope values
 // copied beside K.
 //
-//   * Persistent: one workgroup of 8 waves per CU walks a static share of the
-//     programs (XCD-contiguous, so that the workgroups of one XCD run adjacent
-//     programs and share its L2 copy of W[h] and of the latent rows). Reading
-//     W[h] once per 256 rows halves the L2 traffic of 128-row programs; the 8
-//     waves hold a 256 x 256 output tile (wave w: W rows 128 (w & 1) .. +127 for
-//     cached rows 64 (w >> 1) .. +63).
+//   * Persistent: one workgroup per CU walks a static share of the programs
+//     (XCD-contiguous, so that the workgroups of one XCD run adjacent programs
+//     and share its L2 copy of W[h] and of the latent rows). Reading W[h] once
+//     per 256 rows halves the L2 traffic of 128-row programs.
+//   * 12 waves, three per SIMD: 8 MFMA waves hold the 256 x 256 output tile
+//     (wave w: W rows 128 (w & 1) .. +127 for cached rows 64 (w >> 1) .. +63);
+//     4 copy waves, one per SIMD, issue every copy and keep the books. An MFMA
+//     wave never issues a copy (it would stall behind the busy vector-memory
+//     front end, and its MFMAs with it) and never waits on the memory counter,
+//     so its stores complete on their own.
 //   * Each cached row is walked in slabs of KC columns (64 for an fp8 cache, 32
 //     for bf16): 512 / KC stages multiply a slab of W[h] and of the chunk's 256
 //     latent rows (fp8 kept as bytes and widened exactly to bf16 at the operand
@@ -22,12 +26,11 @@
 //     runs on across program boundaries, so the copy never drains between
 //     programs. The copy rate of a CU is set by the number of distinct cache
 //     lines it requests: a 64-column W slab reads whole 128-byte lines. Each
-//     wave issues its share of every stage's copies and waits for them with
-//     counts of its own; the workgroup barrier then publishes the stage. Each
-//     16-byte piece of a row sits XOR-swizzled by row, so the operand reads hit
-//     distinct banks.
-//   * Wave 0 also copies, ahead of time, each program's page-list window and
-//     the sequence bounds of the programs to come (64 at a time), finds the
+//     copy wave waits for its share of a stage with counts of its own; the
+//     workgroup barrier then publishes the stage. Each 16-byte piece of a row
+//     sits XOR-swizzled by row, so the operand reads hit distinct banks.
+//   * Copy wave 0 also copies, ahead of time, each program's page-list window
+//     and the sequence bounds of the programs to come (64 at a time), finds the
 //     next valid program two programs ahead and works out its row slots, so no
 //     wave ever waits on a dependent load. Results are stored straight from
 //     registers, 8 consecutive output columns per lane.
