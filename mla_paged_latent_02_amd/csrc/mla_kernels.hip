@@ -159,6 +159,7 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(PlanArgs a) {
   __shared__ int32_t cat_wave[4][kCats];
   __shared__ int32_t cat_total[kCats], cat_base[kCats], cat_carry[kCats];
   __shared__ int32_t full_total;
+  __shared__ int32_t wsum_pb[4], wsum_full[4];  // per-wave totals of the tile's two scans
   __shared__ uint32_t bad_or[256];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -172,8 +173,11 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(PlanArgs a) {
   __syncthreads();
   uint32_t bad_acc = 0;
   int32_t my_full = 0;
+  // the first tile's fields, loaded once for both passes (a batch of at most
+  // 256 sequences then costs one round trip for them)
+  const SeqWork w_first = seq_work(a, tid);
   for (int base = 0; base < a.batch; base += 256) {
-    const SeqWork w = seq_work(a, base + tid);
+    const SeqWork w = base == 0 ? w_first : seq_work(a, base + tid);
     bad_acc |= w.bad;
     my_full += w.nfull;
     if (w.cat >= 0) atomicAdd(&cat_total[w.cat], 1);
@@ -196,26 +200,36 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(PlanArgs a) {
   int32_t carry_pb = 0, carry_full = 0;
   for (int base = 0; base < a.batch; base += 256) {
     const int b = base + tid;
-    const SeqWork w = seq_work(a, b);
+    const SeqWork w = base == 0 ? w_first : seq_work(a, b);
     const int32_t contrib = (w.n > 1 ? w.n : 0) * a.num_groups;
-    scan_pb[tid] = contrib;
-    scan_full[tid] = w.nfull;
     int32_t rank = 0;  // among the earlier sequences of this wave with the same class
     for (int k = 0; k < kCats; ++k) {
       const uint64_t m = __builtin_amdgcn_ballot_w64(w.cat == k);
       if (w.cat == k) rank = __popcll(m & ((1ull << lane) - 1));
       if (lane == 0) cat_wave[wave][k] = __popcll(m);
     }
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {  // inclusive Hillis-Steele scans
-      const int32_t v0 = tid >= off ? scan_pb[tid - off] : 0;
-      const int32_t v1 = tid >= off ? scan_full[tid - off] : 0;
-      __syncthreads();
-      scan_pb[tid] += v0;
-      scan_full[tid] += v1;
-      __syncthreads();
+    // inclusive scans of the partial records and the full chunks over the
+    // tile: within each wave by lane shifts, then the earlier waves' totals
+    int32_t v0 = contrib, v1 = w.nfull;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t u0 = __shfl_up(v0, off), u1 = __shfl_up(v1, off);
+      if (lane >= off) {
+        v0 += u0;
+        v1 += u1;
+      }
     }
-    const int32_t my_base = carry_pb + scan_pb[tid] - contrib;
+    if (lane == 63) {
+      wsum_pb[wave] = v0;
+      wsum_full[wave] = v1;
+    }
+    __syncthreads();
+    for (int k = 0; k < wave; ++k) {
+      v0 += wsum_pb[k];
+      v1 += wsum_full[k];
+    }
+    scan_pb[tid] = v0;
+    scan_full[tid] = v1;
+    const int32_t my_base = carry_pb + v0 - contrib;
     t_ctx[tid] = w.ctx;
     t_pb[tid] = w.page_base;
     t_n[tid] = w.n;

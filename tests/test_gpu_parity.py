@@ -207,6 +207,21 @@ def test_merge_paths(batch, heads, ctx, expect_many):
     assert_close(case, out, lse, label=f"merge B={batch} H={heads}")
 
 
+def test_planner_walks_a_batch_of_several_tiles():
+    # 600 sequences: the device planner takes them in three tiles of 256, carrying the
+    # partial-record scan, the full-chunk count and every length class's rank from tile to
+    # tile; lengths (1..320, some exact multiples of the 64-row chunk) put sequences of
+    # every class and of one to five chunks in each tile
+    rng = np.random.default_rng(91)
+    ctx = rng.integers(1, 321, size=600)
+    ctx[::37] = 64 * rng.integers(1, 6, size=len(ctx[::37]))
+    case = make_case(batch=600, seqlen_qo=1, num_heads=16, ctx=[int(c) for c in ctx], page_size=16,
+                     kv_dtype="fp8_e4m3fn", seed=91, pool_pages=int(sum(-(-int(c) // 16) for c in ctx)) + 2)
+    dec, out, lse = run(case, options(force_chunk=64))
+    check_plan_arrays(case, dec)
+    assert_close(case, out, lse, label="600 sequences")
+
+
 def test_one_cu_runs_the_whole_batch():
     # num_cu = 1: the two persistent workgroups of one CU (64-row tiles at occupancy 2) take
     # all of the batch's 43 tasks (chunks of 64 rows) from the counter in turn
