@@ -143,7 +143,7 @@ const char* mla_status_string(mla_status_t status);
 /* Fills *out with the default tunables: wg_per_cu {1, 1, 2, 1} (the 64-row kernel
  * runs at occupancy 2, as the pages' m16x4 kernel does: "HK MLA: MI35x m16x8
  * retune, new m16x4 kernel, page_size + mask support", Summary);
- * chunk_min {256, 256, 256, 128}, chunk_max {8192, 8192, 4096, 6144}, force_chunk 0. */
+ * chunk_min {256, 256, 256, 64}, chunk_max {8192, 8192, 4096, 6144}, force_chunk 0. */
 void mla_plan_options_default(mla_plan_options_t* out);
 
 /*

@@ -70,7 +70,7 @@ const char* mla_status_string(mla_status_t s) {
 void mla_plan_options_default(mla_plan_options_t* out) {
   if (!out) return;
   static const int32_t wg[4] = {1, 1, 2, 1};
-  static const int32_t cmin[4] = {256, 256, 256, 128};
+  static const int32_t cmin[4] = {256, 256, 256, 64};
   static const int32_t cmax[4] = {8192, 8192, 4096, 6144};
   for (int c = 0; c < 4; ++c) {
     out->wg_per_cu[c] = wg[c];

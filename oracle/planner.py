@@ -84,7 +84,7 @@ NUM_XCD = 8
 @dataclass
 class PlanOptions:
     wg_per_cu: List[int] = field(default_factory=lambda: [1, 1, 2, 1])
-    chunk_min: List[int] = field(default_factory=lambda: [256, 256, 256, 128])
+    chunk_min: List[int] = field(default_factory=lambda: [256, 256, 256, 64])
     chunk_max: List[int] = field(default_factory=lambda: [8192, 8192, 4096, 6144])
     force_chunk: int = 0
 

@@ -46,9 +46,9 @@ def test_plan_values_for_the_benchmark_shapes():
     # is capped at 1: want = 2 -> 2600 -> 2624 rows, 2 chunks
     p = reference_plan(128, 4, 16, 5200, 256, kv_dtype="bf16")
     assert (p["chunk_len"], p["max_chunks"], p["num_workgroups"]) == (2624, 2, 256)
-    # small batches of 128 heads at ctx 8192: b = 1: want = 256 -> 32 -> 64 rows, raised to chunk_min = 128,
-    # 64 chunks; b = 5: want = 51 -> 161 -> 192 rows, 43 chunks; b = 16: want = 16 -> 512 rows, 16 chunks
-    for b, C, n in ((1, 128, 64), (5, 192, 43), (16, 512, 16)):
+    # small batches of 128 heads at ctx 8192: b = 1: want = 256 -> 32 -> 64 rows (chunk_min), 128 chunks;
+    # b = 5: want = 51 -> 161 -> 192 rows, 43 chunks; b = 16: want = 16 -> 512 rows, 16 chunks
+    for b, C, n in ((1, 64, 128), (5, 192, 43), (16, 512, 16)):
         p = reference_plan(b, 1, 128, 8192, 256, kv_dtype="fp8_e4m3fn")
         assert (p["tile_rows"], p["chunk_len"], p["max_chunks"]) == (128, C, n), b
     # 256 x 128 heads: want = 1 -> ceil(23333 / 1) rounds to 23360 -> capped at chunk_max = 6144, 4 chunks
