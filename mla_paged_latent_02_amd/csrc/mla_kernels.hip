@@ -357,6 +357,8 @@ __device__ __forceinline__ uint32_t lane_offset(uint32_t off) {
 // min(c_start + blk*BN + w*RPW + r, c_end - 1): rows past the chunk repeat its
 // last row, whose scores are masked. Protocol, per block blk of the loop:
 //   wait(blk); __syncthreads(); advance(blk); ... read stage blk % NS ...
+// (advance(blk) may come later in the iteration: the stage it refills was
+// freed by the barrier, and the loads it issues stay ahead of the next wait)
 // Page ids never come through scalar loads inside the loop: an outstanding
 // scalar load makes the first LDS wait of the block drain everything (the
 // counter is shared and scalar loads return out of order).
@@ -897,12 +899,19 @@ __device__ __forceinline__ void decode_task(const DecodeArgs& a, LDS_PTR(uint8_t
   // only QK^T raised (its PV phase carries the V widening), the others with
   // both phases raised (no effect on the bf16 kernels).
   constexpr bool kPrioPV = !(FP8 && !QF8 && HW == 8);
+  // Where the next block's gather is issued (ring form). Measured per
+  // configuration: the 128-row bf16 kernel is fastest issuing it after its
+  // QK^T MFMAs, so that both waves of a SIMD start their matrix work as soon
+  // as the block is published and the issue overlaps it; the fp8 kernels are
+  // fastest issuing it right after the barrier.
+  constexpr bool kLateGather = !FP8 && HW == 8 && !Cfg::Gather::kVecPages;
 
   for (int blk = 0; blk < nblk; ++blk) {
     gather.wait(blk);
     __syncthreads();
-    gather.advance(blk);
-    // the last block issues no gather: the counter's atomic is the youngest memory operation
+    if constexpr (!kLateGather) gather.advance(blk);
+    // the last block issues no gather, so the counter's round trip queues behind no copy
+    // (the ring form's page-id copy aside)
     if (blk == nblk - 1 && wave == 0 && lane == 0) nxt = take_task(a);
     LDS_PTR(uint8_t) stage = lds + (uint32_t)(blk % NS) * L::kBlockBytes;
     // this wave's 32 rows of the block: main rows at mstage, rope tails at tstage
@@ -989,6 +998,7 @@ __device__ __forceinline__ void decode_task(const DecodeArgs& a, LDS_PTR(uint8_t
     }
 
     __builtin_amdgcn_s_setprio(0);
+    if constexpr (kLateGather) gather.advance(blk);
     // ---- mask, online softmax
     float alpha;
     bool up;
