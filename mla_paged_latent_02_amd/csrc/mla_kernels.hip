@@ -352,8 +352,8 @@ __device__ __forceinline__ uint32_t lane_offset(uint32_t off) {
 }
 
 // Page-gathered loads of one chunk's cache rows, in blocks of BN rows, into
-// an LDS ring of NS stages; the NW waves of the workgroup gather every block
-// together. Row r of wave w's share of block blk is cache row
+// an LDS ring of NS stages; NW waves of the workgroup (waves 0 .. NW-1) gather
+// every block together. Row r of wave w's share of block blk is cache row
 // min(c_start + blk*BN + w*RPW + r, c_end - 1): rows past the chunk repeat its
 // last row, whose scores are masked. Protocol, per block blk of the loop:
 //   wait(blk); __syncthreads(); advance(blk); ... read stage blk % NS ...
@@ -670,7 +670,14 @@ template <bool FP8, int HW, int KW, int NS>
 struct DecodeCfg {
   static constexpr int kWaves = HW * KW;
   static constexpr int kBlockN = 32 * KW;  // cache rows per block
-  using Gather = BlockGather<FP8, kWaves, kBlockN, NS>;
+  // Waves that issue the gather. The 128-row kernels (two waves per SIMD of
+  // one workgroup) gather with one wave per SIMD, each taking twice the rows,
+  // so that the other wave of each SIMD goes straight from the barrier to its
+  // QK^T MFMAs and the pair falls out of step (measured: ragged fp8 decode
+  // 832 -> 751 us, dense fp8 171.5 -> 162.2, dense bf16 155.2 -> 153.5; the
+  // 64-row kernel, whose two waves per SIMD come from two workgroups, lost).
+  static constexpr int kGatherWaves = (HW == 8 && KW == 1) ? kWaves / 2 : kWaves;
+  using Gather = BlockGather<FP8, kGatherWaves, kBlockN, NS>;
   using L = typename Gather::L;
   static constexpr int kRingBytes = NS * L::kBlockBytes + Gather::kPidRingBytes;  // stages, then page ids
   // Merge area after the loop: 16 x 512 fp32 outputs, then a max and a sum per head, of every
@@ -754,7 +761,8 @@ __device__ __forceinline__ void decode_task(const DecodeArgs& a, LDS_PTR(uint8_t
   typename Cfg::Gather gather(a, (uint32_t)(uintptr_t)lds, (uint32_t)(uintptr_t)lds + NS * L::kBlockBytes, c_start,
                               c_end, page_base, wave, lane);
   const int nblk = gather.nblk;
-  gather.prefetch_ids();  // in flight with the query loads below
+  const bool gw = wave < Cfg::kGatherWaves;  // this wave issues gather copies (uniform)
+  if (gw) gather.prefetch_ids();  // in flight with the query loads below
 
   // ---- query fragments (B operand of S^T = K Q^T), resident for the whole chunk.
   // bf16 cache: qf[t] holds d = 32t + 8*g4 .. +7 (18 fragments).
@@ -890,7 +898,7 @@ __device__ __forceinline__ void decode_task(const DecodeArgs& a, LDS_PTR(uint8_t
   // the live context length came with the query: the plan holds for the lengths it was made with
   asm volatile("" ::"s"(live_ctx));
   if (live_ctx != ctx && chunk == 0 && grp == 0 && wave == 0 && lane == 0) atomicOr(a.status, MLA_DEV_STALE_PLAN);
-  gather.start();
+  if (gw) gather.start();
   const float sscale = a.score_scale_log2;
   // Wave priority: two waves share each SIMD, and while one runs its softmax
   // (and, for an fp8 cache, widens V) the other should keep the matrix pipe
@@ -907,9 +915,9 @@ __device__ __forceinline__ void decode_task(const DecodeArgs& a, LDS_PTR(uint8_t
   constexpr bool kLateGather = !FP8 && HW == 8 && !Cfg::Gather::kVecPages;
 
   for (int blk = 0; blk < nblk; ++blk) {
-    gather.wait(blk);
+    if (gw) gather.wait(blk);
     __syncthreads();
-    if constexpr (!kLateGather) gather.advance(blk);
+    if (!kLateGather && gw) gather.advance(blk);
     // the last block issues no gather, so the counter's round trip queues behind no copy
     // (the ring form's page-id copy aside)
     if (blk == nblk - 1 && wave == 0 && lane == 0) nxt = take_task(a);
@@ -998,7 +1006,7 @@ __device__ __forceinline__ void decode_task(const DecodeArgs& a, LDS_PTR(uint8_t
     }
 
     __builtin_amdgcn_s_setprio(0);
-    if constexpr (kLateGather) gather.advance(blk);
+    if (kLateGather && gw) gather.advance(blk);
     // ---- mask, online softmax
     float alpha;
     bool up;
@@ -1052,7 +1060,7 @@ __device__ __forceinline__ void decode_task(const DecodeArgs& a, LDS_PTR(uint8_t
     }
     if constexpr (kPrioPV) __builtin_amdgcn_s_setprio(0);
   }
-  gather.report(a.status);
+  if (gw) gather.report(a.status);
 
   // ---- epilogue. Each head tile has KW partial states (m_ref, l, o_acc) over
   // disjoint row sets, each relative to its own reference max; with KW > 1
