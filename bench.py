@@ -349,9 +349,11 @@ def roofline_for(nbytes, flops, seconds):
             "frac": tf / MFMA_BF16_PEAK_TFLOPS}
 
 
-def measure_decode(case, workload, steps, warmup, use_flush, plan_reps=20):
+def measure_decode(case, workload, steps, warmup, use_flush, plan_reps=20, warm_s=0.0):
     """Times one workload: plan (device launch, event pairs), then `steps` calls of decode + merge with a
-    read flush before each. Returns the raw measurements and derived rates as a dict."""
+    read flush before each. After the `warmup` calls, untimed calls continue until `warm_s` seconds have
+    passed (the per-config lines follow an idle stretch of the GPU, whose clocks then take a while to
+    come back up). Returns the raw measurements and derived rates as a dict."""
     import numpy as np
     import torch
 
@@ -392,6 +394,13 @@ def measure_decode(case, workload, steps, warmup, use_flush, plan_reps=20):
             torch.sum(flush, dim=0, out=sink)
         step()
     torch.cuda.synchronize()
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < warm_s:
+        for _ in range(5):
+            if flush is not None:
+                torch.sum(flush, dim=0, out=sink)
+            step()
+        torch.cuda.synchronize()
     # Timed loop 1 (the reported value): one event pair around each whole call, nothing in between.
     call_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     wall0 = time.perf_counter()
@@ -510,7 +519,8 @@ def main():
             del case
             case = make_case(**WORKLOADS[name])
             configs[name] = config_summary(case, measure_decode(case, name, args.config_steps,
-                                                                min(args.warmup, 5), not args.no_flush))
+                                                                min(args.warmup, 5), not args.no_flush,
+                                                                warm_s=0.2))
             print(json.dumps({"config_done": name, "us_per_call": configs[name]["us_per_call"]}),
                   file=sys.stderr, flush=True)
 
