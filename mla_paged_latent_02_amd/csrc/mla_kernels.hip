@@ -278,28 +278,46 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(PlanArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS block layout (one ring stage, BN cache rows):
-//   main region: row r at r*kMainStride holds the 512 latent elements (the V
-//                part); the stride is padded by 32 bytes (8 banks);
-//   tail region: row r at kTailBase + r*kTailBytes holds the 64 rope elements
-//                (16-byte slots, physical slot p holds logical slot
-//                p ^ tail_xor(r)).
-// MFMA row m of K score tile nt is LDS row nt*16 + m. Measured on gfx950 with
-// 8 waves: a K fragment read (16 rows x 64 bytes) takes 4.6-4.8 clocks per
-// instruction at this stride against 4.5 for a contiguous read (8.0 with a
-// 16-byte pad), and the transposed V reads stay at 3.2-4.0 clocks.
+// LDS block layout (one ring stage, BN cache rows; BN is a multiple of 32):
+//   main region, bf16: row r at r*kMainStride holds its 512 latent elements
+//                (the V part); the 1024-byte row is padded by 32 bytes (8 banks);
+//   main region, fp8: the rows come in pairs, rows p and p + 8 of each
+//                16-row group g forming pair P = 8g + p at P*kMainStride, the
+//                first row in bytes 0..511 of the pair and the second in
+//                512..1023, so that one 64-lane copy moves both rows and the
+//                rows a wave copies stay within 16-row groups (a page of 16
+//                rows holds them). Rows r and r + 16 share banks in transposed
+//                V reads, as at any pitch that is a multiple of 16 bytes; those
+//                conflicts are off the critical path;
+//   tail region: the 64 rope elements of each row, kTailBytes apart from
+//                kTailBase in copy order (the row at position pos is
+//                row_at(pos): bf16 pos, fp8 the first or second row of pair
+//                pos / 2 as pos is even or odd), in 16-byte slots (physical
+//                slot j holds logical slot j ^ tail_xor(pos)).
+// MFMA row m of K score tile nt is slice row nt*16 + m (fp8: row m / 8 of pair
+// m % 8 of the tile's group). Measured on gfx950 with 8 waves: a K fragment
+// read (16 rows x 64 bytes) takes 4.6-4.8 clocks per instruction at the bf16
+// stride against 4.5 for a contiguous read (8.0 with a 16-byte pad), and the
+// transposed V reads stay at 3.2-4.0 clocks.
 template <bool FP8, int BN>
 struct RowLayout {
+  static_assert(BN % 32 == 0, "32-row slices");
   static constexpr int kElem = FP8 ? 1 : 2;
   static constexpr int kRowBytes = kRowDim * kElem;      // 576 or 1152 in the cache
   static constexpr int kMainBytes = kLatentDim * kElem;  // 512 or 1024
-  static constexpr int kMainStride = kMainBytes + 32;
+  static constexpr int kMainStride = 1024 + 32;          // bf16 row pitch, fp8 pair pitch
+  static constexpr int kTileStride = (FP8 ? 8 : 16) * kMainStride;  // main bytes of 16 rows
+  static constexpr int kSliceBytes = 2 * kTileStride;                // and of 32
   static constexpr int kTailBytes = 64 * kElem;          // 64 or 128
   static constexpr int kTailSlots = kTailBytes / 16;     // 4 or 8
-  static constexpr int kTailBase = BN * kMainStride;
+  static constexpr int kTailBase = BN / 32 * kSliceBytes;
   static constexpr int kBlockBytes = kTailBase + BN * kTailBytes;
-  // the tail row stride spans kTailBytes/4 banks; the row bits above that pick the xor
-  static __device__ __forceinline__ int tail_xor(int r) { return FP8 ? ((r >> 2) & 3) : ((r >> 1) & 7); }
+  // the tail row stride spans kTailBytes/4 banks; the position bits above that pick the xor
+  static __device__ __forceinline__ int tail_xor(int pos) { return FP8 ? ((pos >> 2) & 3) : ((pos >> 1) & 7); }
+  // the block row whose copy comes at position pos
+  static __device__ __forceinline__ int row_at(int pos) {
+    return FP8 ? 16 * (pos >> 4) + ((pos >> 1) & 7) + 8 * (pos & 1) : pos;
+  }
 };
 
 __device__ __forceinline__ u32x4_t lds_b128(LDS_PTR(uint8_t) base, uint32_t off) {
@@ -353,9 +371,12 @@ __device__ __forceinline__ uint32_t lane_offset(uint32_t off) {
 
 // Page-gathered loads of one chunk's cache rows, in blocks of BN rows, into
 // an LDS ring of NS stages; NW waves of the workgroup (waves 0 .. NW-1) gather
-// every block together. Row r of wave w's share of block blk is cache row
-// min(c_start + blk*BN + w*RPW + r, c_end - 1): rows past the chunk repeat its
-// last row, whose scores are masked. Protocol, per block blk of the loop:
+// every block together. Wave w copies the rows at positions w*RPW .. w*RPW +
+// RPW - 1 of the block's copy order (RowLayout), the r-th of them being cache
+// row min(c_start + blk*BN + row_at(w*RPW + r), c_end - 1): rows past the
+// chunk repeat its last row, whose scores are masked. An fp8 row pair (two
+// consecutive positions) takes one copy instruction, a bf16 row one.
+// Protocol, per block blk of the loop:
 //   wait(blk); __syncthreads(); advance(blk); ... read stage blk % NS ...
 // (advance(blk) may come later in the iteration: the stage it refills was
 // freed by the barrier, and the loads it issues stay ahead of the next wait)
@@ -379,10 +400,14 @@ struct BlockGather {
   static constexpr int RPW = BN / NW;  // rows each wave gathers per block
   static constexpr int kTailRowsPerInst = 64 / L::kTailSlots;
   static constexpr int kTailInsts = (RPW + kTailRowsPerInst - 1) / kTailRowsPerInst;
-  static constexpr int kDmaInsts = RPW + kTailInsts;  // gather instructions per wave per block
+  static constexpr int kMainInsts = FP8 ? RPW / 2 : RPW;
+  static constexpr int kDmaInsts = kMainInsts + kTailInsts;  // gather instructions per wave per block
   static constexpr bool kVecPages = NS == 2;
   static constexpr int kPidRingBytes = kVecPages ? 0 : NS * BN * 4;
   static_assert(RPW >= 1 && BN % NW == 0, "row split");
+  // a wave's fp8 pairs fill part of one 16-row group or whole groups, so that
+  // its first and last copies hold its lowest and highest rows
+  static_assert(!FP8 || (RPW % 2 == 0 && (16 % RPW == 0 || RPW % 16 == 0)), "fp8 pairs of a wave");
   static_assert(kVecPages || RPW % 4 == 0, "page ids are read four at a time");
   static_assert((NS - 2) * (kDmaInsts + 1) <= 63, "vmcnt range");
 
@@ -390,7 +415,7 @@ struct BlockGather {
   const int32_t* page_ids;
   int64_t num_pages;
   uint32_t magic, lds_base, pid_base;
-  int c_start, c_end, nblk, page_base, P, wave, lane, tslot, trow, my_row;
+  int c_start, c_end, nblk, page_base, P, wave, lane, tslot, trow;
   bool bad_page;
   int v_page;  // two stages: lane r < RPW holds the page id of row r of the next block
 
@@ -412,7 +437,6 @@ struct BlockGather {
         lane(lane_),
         tslot(lane_ % L::kTailSlots),
         trow(lane_ / L::kTailSlots),
-        my_row(lane_ < RPW ? lane_ : RPW - 1),
         bad_page(false),
         v_page(0) {}
 
@@ -425,7 +449,14 @@ struct BlockGather {
     }
   }
   __device__ __forceinline__ int row_kv(int blk, int r) const {
-    return min(c_start + blk * BN + wave * RPW + r, c_end - 1);
+    return min(c_start + blk * BN + L::row_at(wave * RPW + r), c_end - 1);
+  }
+  // the copy whose page id lane l loads: min(l, RPW - 1). For an fp8 cache its
+  // row is formed where it is used: held across the block loop instead, it is
+  // the value the register allocator spills first in the two-waves-per-SIMD
+  // fp8 kernels.
+  __device__ __forceinline__ int my_row() const {
+    return min(FP8 ? (int)lane_offset((uint32_t)lane) : lane, RPW - 1);
   }
   __device__ __forceinline__ int checked(int pg) {
     if ((uint32_t)pg >= (uint64_t)num_pages) {
@@ -434,13 +465,19 @@ struct BlockGather {
     }
     return pg;
   }
-  // main part of row r: one instruction; lane l fetches the row's 16-byte slot l
-  // (bf16: 64 slots; fp8: 32 slots, the caller masks off the upper half of the wave)
-  __device__ __forceinline__ void issue_main_row(int blk, int r, int slot_s) const {
+  // main part of the wave's j-th copy, one instruction. bf16: row j of the
+  // wave (slot s0), lane l fetches its 16-byte slot l. fp8: the pair of rows
+  // 2j and 2j + 1 of the wave (slots s0, s1), lanes 0-31 fetch the first row's
+  // 32 slots, lanes 32-63 the second row's.
+  __device__ __forceinline__ void issue_main(int blk, int j, int s0, int s1) const {
     const uint32_t stage_off = (uint32_t)(blk % NS) * L::kBlockBytes;
-    const uint8_t* src = cache + (int64_t)slot_s * L::kRowBytes + (lane << 4);
+    const uint8_t* src;
+    if constexpr (FP8)
+      src = cache + (int64_t)(lane < 32 ? s0 : s1) * L::kRowBytes + ((lane & 31) << 4);
+    else
+      src = cache + (int64_t)s0 * L::kRowBytes + (lane << 4);
     const uint32_t dst =
-        __builtin_amdgcn_readfirstlane(lds_base + stage_off + (uint32_t)((wave * RPW + r) * L::kMainStride));
+        __builtin_amdgcn_readfirstlane(lds_base + stage_off + (uint32_t)((wave * kMainInsts + j) * L::kMainStride));
     dma16(src, dst);
   }
   // rope tails: instruction m covers kTailRowsPerInst rows x kTailSlots slots;
@@ -461,23 +498,26 @@ struct BlockGather {
   // ring stages: copy the page ids of block j (clamped to the chunk) into the ring
   __device__ __forceinline__ void pid_copy(int j) const {
     int q, rem;
-    page_pos(row_kv(min(j, nblk - 1), my_row), q, rem);
+    page_pos(row_kv(min(j, nblk - 1), my_row()), q, rem);
     if (lane < RPW) dma4(page_ids + page_base + q, __builtin_amdgcn_readfirstlane(pid_slot(j)));
   }
   // two stages: load the page ids of block blk into v_page
   __device__ __forceinline__ void fetch_v(int blk) {
     int q, rem;
-    page_pos(row_kv(blk, my_row), q, rem);
+    page_pos(row_kv(blk, my_row()), q, rem);
     v_page = page_ids[page_base + q];
   }
   __device__ __forceinline__ void issue(int blk) {
     if constexpr (kVecPages) {
       int q, rem;
-      page_pos(row_kv(blk, my_row), q, rem);
+      page_pos(row_kv(blk, my_row()), q, rem);
       const int slot_v = checked(v_page) * P + rem;
-      if (FP8 ? lane < 32 : true) {
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) issue_main_row(blk, r, __builtin_amdgcn_readlane(slot_v, r));
+      for (int j = 0; j < kMainInsts; ++j) {
+        if constexpr (FP8)
+          issue_main(blk, j, __builtin_amdgcn_readlane(slot_v, 2 * j), __builtin_amdgcn_readlane(slot_v, 2 * j + 1));
+        else
+          issue_main(blk, j, __builtin_amdgcn_readlane(slot_v, j), 0);
       }
 #pragma unroll
       for (int m = 0; m < kTailInsts; ++m)
@@ -492,8 +532,9 @@ struct BlockGather {
 #pragma unroll
         for (int k = 0; k < 4; ++k) pid[r4 + k] = __builtin_amdgcn_readfirstlane((int)v[k]);
       }
-      // slots of the wave's rows; when one page holds them all (the rows are
-      // consecutive cache rows of a chunk), one lookup gives consecutive slots
+      // slots of the wave's rows; when one page holds them all (they lie
+      // between the rows of its first and last copies, and a page holds
+      // consecutive cache rows), one lookup gives them all
       int slot[RPW];
       const int kv_a = __builtin_amdgcn_readfirstlane(row_kv(blk, 0));
       const int kv_b = __builtin_amdgcn_readfirstlane(row_kv(blk, RPW - 1));
@@ -511,9 +552,12 @@ struct BlockGather {
           slot[r] = checked(pid[r]) * P + rem;
         }
       }
-      if (FP8 ? lane < 32 : true) {  // one exec mask for all the wave's main rows
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) issue_main_row(blk, r, slot[r]);
+      for (int j = 0; j < kMainInsts; ++j) {
+        if constexpr (FP8)
+          issue_main(blk, j, slot[2 * j], slot[2 * j + 1]);
+        else
+          issue_main(blk, j, slot[j], 0);
       }
 #pragma unroll
       for (int m = 0; m < kTailInsts; ++m) {
@@ -877,8 +921,11 @@ __device__ __forceinline__ void decode_task(const DecodeArgs& a, LDS_PTR(uint8_t
   for (int nt = 0; nt < 32; ++nt) o_acc[nt] = f32x4_t{0, 0, 0, 0};
 
   // Per-lane LDS offsets that do not change over the loop; each access adds a
-  // compile-time immediate.
-  const uint32_t k_main_base = (uint32_t)i16 * L::kMainStride + (uint32_t)g4 * 16;
+  // compile-time immediate. K row i16 of score tile nt sits at k_main_base +
+  // nt*kTileStride (fp8: row i16 / 8 of pair i16 % 8 of the tile's group).
+  const uint32_t k_main_base =
+      (FP8 ? (uint32_t)(i16 & 7) * L::kMainStride + (uint32_t)(i16 >> 3) * 512u : (uint32_t)i16 * L::kMainStride) +
+      (uint32_t)g4 * 16;
   // V^T reads of the P^T fragment: element e < 4 is row 4g4 + e of the wave's
   // 32, e >= 4 is 16 + 4g4 + e - 4 (the order of the score rows in P^T).
   uint32_t v_base_lo, v_base_hi;
@@ -886,7 +933,7 @@ __device__ __forceinline__ void decode_task(const DecodeArgs& a, LDS_PTR(uint8_t
     // supplier lane (k = i16/2, c = i16%2) reads element k's row, bytes 8c of the column tile
     const int k = i16 >> 1, c = i16 & 1;
     const int row = k < 4 ? 4 * g4 + k : 16 + 4 * g4 + k - 4;
-    v_base_lo = (uint32_t)row * L::kMainStride + 8u * c;
+    v_base_lo = (uint32_t)(8 * (row >> 4) + (row & 7)) * L::kMainStride + (uint32_t)((row >> 3) & 1) * 512u + 8u * c;
     v_base_hi = v_base_lo;
   } else {
     // supplier lane (k = i16/4, c = i16%4) reads rows of elements k and 4+k, columns 4c..4c+3
@@ -923,7 +970,7 @@ __device__ __forceinline__ void decode_task(const DecodeArgs& a, LDS_PTR(uint8_t
     if (blk == nblk - 1 && wave == 0 && lane == 0) nxt = take_task(a);
     LDS_PTR(uint8_t) stage = lds + (uint32_t)(blk % NS) * L::kBlockBytes;
     // this wave's 32 rows of the block: main rows at mstage, rope tails at tstage
-    LDS_PTR(uint8_t) mstage = stage + (uint32_t)(kw * 32 * L::kMainStride);
+    LDS_PTR(uint8_t) mstage = stage + (uint32_t)(kw * L::kSliceBytes);
     LDS_PTR(uint8_t) tstage = stage + (uint32_t)(L::kTailBase + kw * 32 * L::kTailBytes);
     const int kv0 = c_start + blk * BN + kw * 32;
 
@@ -940,7 +987,9 @@ __device__ __forceinline__ void decode_task(const DecodeArgs& a, LDS_PTR(uint8_t
 #pragma unroll
         for (int c = 0; c < QC; ++c) sch[nt][c] = f32x4_t{0, 0, 0, 0};
       auto tail_read = [&](int nt, int slot) -> u32x4_t {  // logical 16-byte slot of the row's rope tail
-        return lds_b128(tstage, (uint32_t)((nt * 16 + i16) * L::kTailBytes) + ((uint32_t)(slot ^ L::tail_xor(i16)) << 4));
+        // copy position of slice row nt*16 + i16
+        const int pos = FP8 ? 16 * nt + 2 * (i16 & 7) + (i16 >> 3) : nt * 16 + i16;
+        return lds_b128(tstage, (uint32_t)(pos * L::kTailBytes) + ((uint32_t)(slot ^ L::tail_xor(pos)) << 4));
       };
       if constexpr (FP8) {
         // Unit u < 8 = (block kb = u / 2, tile nt = u % 2): the lane's two 16-byte
@@ -950,7 +999,7 @@ __device__ __forceinline__ void decode_task(const DecodeArgs& a, LDS_PTR(uint8_t
         i32x8_t ku[KD];
         auto kunit = [&](int u) -> i32x8_t {
           if (u < 8) {
-            const uint32_t off = k_main_base + (uint32_t)((u & 1) * 16 * L::kMainStride + (u >> 1) * 128);
+            const uint32_t off = k_main_base + (uint32_t)((u & 1) * L::kTileStride + (u >> 1) * 128);
             const u32x4_t lo = lds_b128(mstage, off), hi = lds_b128(mstage, off + 64);
             return __builtin_bit_cast(i32x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           }
@@ -984,7 +1033,7 @@ __device__ __forceinline__ void decode_task(const DecodeArgs& a, LDS_PTR(uint8_t
         auto kread = [&](int i) -> u32x4_t {
           const int step = i / 2, nt = i % 2;
           if (step < 16)
-            return lds_b128(mstage, k_main_base + (uint32_t)(nt * 16 * L::kMainStride + step * 64));
+            return lds_b128(mstage, k_main_base + (uint32_t)(nt * L::kTileStride + step * 64));
           return tail_read(nt, 4 * (step - 16) + g4);
         };
 #pragma unroll
