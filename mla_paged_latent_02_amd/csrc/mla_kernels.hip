@@ -413,7 +413,7 @@ struct BlockGather {
 
   const uint8_t* cache;
   const int32_t* page_ids;
-  int64_t num_pages;
+  uint32_t page_lim;  // page ids (int32) at or above this, as unsigned, are outside the pool
   uint32_t magic, lds_base, pid_base;
   int c_start, c_end, nblk, page_base, P, wave, lane, tslot, trow;
   bool bad_page;
@@ -424,7 +424,8 @@ struct BlockGather {
                                          int c_end_, int page_base_, int wave_, int lane_)
       : cache(a.cache),
         page_ids(a.kv_page_indices),
-        num_pages(a.num_pages),
+        // min(num_pages, 2^31): a pool of 2^31 pages or more holds every non-negative id
+        page_lim((uint32_t)(a.num_pages < 0x80000000LL ? a.num_pages : 0x80000000LL)),
         magic(a.page_div_magic),
         lds_base(lds_base_),
         pid_base(pid_lds),
@@ -459,7 +460,7 @@ struct BlockGather {
     return min(FP8 ? (int)lane_offset((uint32_t)lane) : lane, RPW - 1);
   }
   __device__ __forceinline__ int checked(int pg) {
-    if ((uint32_t)pg >= (uint64_t)num_pages) {
+    if ((uint32_t)pg >= page_lim) {
       bad_page = true;
       pg = 0;
     }
@@ -544,6 +545,9 @@ struct BlockGather {
         const int s0 = checked(pid[0]) * P + rema;
 #pragma unroll
         for (int r = 0; r < RPW; ++r) slot[r] = s0 + (__builtin_amdgcn_readfirstlane(row_kv(blk, r)) - kv_a);
+      } else if (P == 1) {  // a page per row: the slot is the page id
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) slot[r] = checked(pid[r]);
       } else {
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
