@@ -333,6 +333,14 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory");
 }
 
+// The same from a uniform 64-bit base held in scalar registers plus a 32-bit
+// per-lane offset (the lane's address is sbase + voff), so that no per-lane
+// 64-bit address has to be formed for a copy whose lanes share one row.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory");
+}
+
 // The same for 4 bytes per lane (global_load_lds_dword): lane i lands at lds_addr + 4*lane.
 __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds_addr) : "memory");
@@ -467,19 +475,17 @@ struct BlockGather {
     return pg;
   }
   // main part of the wave's j-th copy, one instruction. bf16: row j of the
-  // wave (slot s0), lane l fetches its 16-byte slot l. fp8: the pair of rows
+  // wave (slot s0, a uniform base), lane l fetches its 16-byte slot l. fp8: the pair of rows
   // 2j and 2j + 1 of the wave (slots s0, s1), lanes 0-31 fetch the first row's
   // 32 slots, lanes 32-63 the second row's.
   __device__ __forceinline__ void issue_main(int blk, int j, int s0, int s1) const {
     const uint32_t stage_off = (uint32_t)(blk % NS) * L::kBlockBytes;
-    const uint8_t* src;
-    if constexpr (FP8)
-      src = cache + (int64_t)(lane < 32 ? s0 : s1) * L::kRowBytes + ((lane & 31) << 4);
-    else
-      src = cache + (int64_t)s0 * L::kRowBytes + (lane << 4);
     const uint32_t dst =
         __builtin_amdgcn_readfirstlane(lds_base + stage_off + (uint32_t)((wave * kMainInsts + j) * L::kMainStride));
-    dma16(src, dst);
+    if constexpr (FP8)
+      dma16(cache + (int64_t)(lane < 32 ? s0 : s1) * L::kRowBytes + ((lane & 31) << 4), dst);
+    else
+      dma16s(cache + (int64_t)s0 * L::kRowBytes, (uint32_t)lane << 4, dst);
   }
   // rope tails: instruction m covers kTailRowsPerInst rows x kTailSlots slots;
   // sv is the slot of this lane's row
