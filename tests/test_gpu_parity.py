@@ -338,6 +338,31 @@ def test_short_page_list_and_bad_page_ids_are_flagged_not_read():
     assert_close(case2, out, lse, batches=[0], label="short page list next door")
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("kv_dtype,heads", [("bf16", 128), ("fp8_e4m3fn", 32)])
+def test_page_id_bounds_at_one_row_per_page(kv_dtype, heads):
+    # one row per page on ring-gather kernels (128-row bf16, 32-row fp8): the pool's last slot is a
+    # valid page and is read; one past it and -1 are flagged, clamped to page 0, and leave the
+    # other sequence exact
+    import mla_paged_latent_02_amd as mla
+    case = make_case(batch=2, seqlen_qo=1, num_heads=heads, ctx=[90, 70], page_size=1, kv_dtype=kv_dtype,
+                     seed=81)
+    case.kv_page_indices[case.kv_indptr[0] + 5] = case.num_slots - 1
+    dec, out, lse = run(case)
+    _, _, status = mla.read_plan_arrays(dec.plan, dec.workspace)
+    assert not status[0] & mla.DEV_PAGE_OUT_OF_RANGE
+    assert_close(case, out, lse, label="last slot of the pool")
+    good = case.kv_page_indices.copy()
+    for bad in (case.num_slots, -1):
+        case.kv_page_indices = good.copy()
+        case.kv_page_indices[case.kv_indptr[1] + 3] = bad
+        dec, out, lse = run(case)
+        _, _, status = mla.read_plan_arrays(dec.plan, dec.workspace)
+        assert status[0] & mla.DEV_PAGE_OUT_OF_RANGE, bad
+        case.kv_page_indices = good
+        assert_close(case, out, lse, batches=[0], label=f"page id {bad} in the other sequence")
+
+
 # ------------------------------------------------------------------ full-size workloads, every sequence
 # The oracle computes each sequence exactly (numpy fp64 on the host cores): every output row of
 # every benchmark workload is compared, not a sample.
